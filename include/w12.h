@@ -1,0 +1,164 @@
+/*
+ * w12.h - C ABI of libw12: the W12 lossless 12-bit BF16 weight format on MI355X (gfx950).
+ *
+ * W12 (SpecPilot, arXiv 2611.02501; summary page, method bullet of section 4.1, and the
+ * news article part "(1) W12") stores each BF16 weight of an output channel as
+ *   sign (1 bit) | exponent offset inside a 16-binade window chosen per channel (4 bits) |
+ *   mantissa (7 bits),
+ * and keeps weights outside the window, zeros, denormals and inf/NaN in an exact escape
+ * list.  Every decoded tensor is checked bit for bit at load time (summary page, result
+ * bullet of section 4.1), and the GEMM decodes the records in registers and reduces its
+ * split in a fixed order, so it is deterministic (method bullet of section 4.1).
+ *
+ * Logical format (what every result is defined on):
+ *   base[n]        window base exponent field b_n in 1..239; the window is [b_n, b_n+15].
+ *                  b_n is the smallest b that maximises the number of in-window weights.
+ *   rec[n][k]      (s << 11) | ((e - b_n) << 7) | m for in-window weights, 0 at escapes.
+ *   esc_ptr[N+1]   exclusive prefix sum of per-channel escape counts (esc_ptr[0] = 0).
+ *   esc[E]         (k << 16) | bf16_bits, channel after channel, ascending k in a channel.
+ *
+ * Physical layout W12_LAYOUT_RB16_K16 (this library's choice; w12_unpack_records gives the
+ * logical records back).  Rows are grouped in row blocks of 16 (Nb = ceil(N/16)) and k in
+ * chunks of 16 (Kc = ceil(K/16)); rows >= N and k >= K are padding with record 0.
+ *   hi: uint8 [Nb][Kc][16 rows][16]  byte j of row r = rec >> 4 = s | off(4) | m[6:4]
+ *       (also the nested 8-bit view of each weight).
+ *   lo: uint8 [Nb][Kc][16 rows][8]   the low mantissa nibbles rec & 0xF of the 16 weights:
+ *       byte 4d+i (d = 0,1; i = 0..3) holds weight 8d+i in its high nibble and weight
+ *       8d+4+i in its low nibble.
+ *
+ * Conventions for every call:
+ *   - All pointers are device pointers owned by the caller; the library never allocates
+ *     and never frees.  BF16 data is passed as uint16_t bit patterns.
+ *   - Every call that takes a stream only validates on the host and enqueues kernels on
+ *     that stream; it returns before the GPU work finishes.  No call synchronises.
+ *   - Return value: W12_OK (0) or a negative W12_ERR_* code.  Arguments are validated
+ *     before any HIP call; on an error nothing is enqueued.  w12_last_error() gives a
+ *     message for the last failing call of the calling thread.
+ *   - Row pitches (ldw, ldx, ldo, ldr, ldy) are in elements.  BF16 matrices read or
+ *     written with vector accesses (W, X, decode output, verify reference) need a
+ *     16-byte aligned base pointer and a pitch that is a multiple of 8 elements.
+ *   - Shapes: 1 <= N <= 2^24, 1 <= K <= 65536 (k fits the 16-bit field of an escape
+ *     entry), N*K < 2^32 (escape counts are 32-bit); 1 <= M <= 4096 for the GEMM.
+ */
+#ifndef W12_H
+#define W12_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W12_OK 0
+#define W12_ERR_INVALID_ARG (-1)          /* null pointer, bad pitch, bad descriptor        */
+#define W12_ERR_UNSUPPORTED_SHAPE (-2)    /* N, K or M outside the supported ranges          */
+#define W12_ERR_WORKSPACE_TOO_SMALL (-3)  /* ws_bytes below w12_gemm_workspace_size          */
+#define W12_ERR_HIP (-4)                  /* a HIP runtime call or kernel launch failed      */
+#define W12_ERR_MISALIGNED (-5)           /* a vector-accessed pointer or pitch is unaligned */
+
+#define W12_LAYOUT_RB16_K16 1
+
+/* Descriptor of an encoded tensor.  All arrays are device memory owned by the caller. */
+typedef struct w12_tensor {
+  int32_t N, K;          /* logical shape of W[N][K]                                     */
+  int32_t layout;        /* W12_LAYOUT_RB16_K16                                          */
+  int32_t reserved;      /* must be 0                                                    */
+  int64_t num_escapes;   /* E = esc_ptr[N]                                               */
+  uint8_t *base;         /* [N]                                                          */
+  uint8_t *hi;           /* [w12_layout_bytes().hi_bytes]                                */
+  uint8_t *lo;           /* [w12_layout_bytes().lo_bytes]                                */
+  uint32_t *esc_ptr;     /* [N+1]                                                        */
+  uint32_t *esc;         /* [E] (may be NULL when E == 0)                                */
+} w12_tensor;
+
+/* Sizes of the hi and lo planes of the physical layout for W[N][K].  Host only. */
+int w12_layout_bytes(int32_t N, int32_t K, uint64_t *hi_bytes, uint64_t *lo_bytes);
+
+/*
+ * Encode pass 1 (window choice, summary page method bullet of section 4.1; news article
+ * "(1) W12": exponents cluster within a channel).  For every channel n of the BF16 matrix
+ * W (row pitch ldw) computes base[n] (or copies forced_base[n] when forced_base is not
+ * NULL - a test hook; each value must be in 1..239) and writes
+ *   esc_ptr[0] = 0, esc_ptr[n+1] = sum_{i<=n} (K - in-window count of channel i).
+ * The caller reads E = esc_ptr[N] back to size esc[] before w12_encode_emit.
+ * forced_base values outside 1..239 are clamped into range by the kernel (the host
+ * cannot inspect device memory without synchronising).
+ */
+int w12_encode_count(const uint16_t *W, int32_t N, int32_t K, int64_t ldw,
+                     const uint8_t *forced_base, uint8_t *base, uint32_t *esc_ptr,
+                     hipStream_t stream);
+
+/*
+ * Encode pass 2 (records and escape list, summary page method bullet of section 4.1).
+ * Reads W and t->base / t->esc_ptr written by w12_encode_count and writes t->hi, t->lo
+ * (padding included) and t->esc.  Escapes of a channel are compacted in ascending k with
+ * wavefront prefix sums.  t->num_escapes must equal esc_ptr[N].
+ */
+int w12_encode_emit(const uint16_t *W, int64_t ldw, const w12_tensor *t, hipStream_t stream);
+
+/*
+ * Full-tensor decode (summary page result bullet of section 4.1: decoded tensors are the
+ * original weights bit for bit).  Writes out[n][k] (row pitch ldo) for n < N, k < K.
+ * The escape list must be well formed (ascending k < K per channel); w12_verify checks it.
+ */
+int w12_decode(const w12_tensor *t, uint16_t *out, int64_t ldo, hipStream_t stream);
+
+/*
+ * Load-time bit-for-bit check (summary page result bullet of section 4.1).  Decodes t and
+ * compares with ref (row pitch ldr).  Writes, on the device,
+ *   d_result[0] = number of positions (n,k) whose decoded bits differ from ref[n][k]
+ *                 plus the number of malformed escape entries (k >= K, k not strictly
+ *                 ascending within a channel, non-zero record under an escape) plus
+ *                 the number of inconsistent pointers (esc_ptr[0] != 0, a decreasing
+ *                 step, esc_ptr[N] != num_escapes);
+ *   d_result[1] = smallest flat index n*K + k of a differing position, or
+ *                 0xFFFFFFFFFFFFFFFF if there is none.
+ * d_result must point to 2 device uint64 values; the call resets them first.
+ */
+int w12_verify(const w12_tensor *t, const uint16_t *ref, int64_t ldr,
+               unsigned long long *d_result, hipStream_t stream);
+
+/* Test aid: writes the logical 12-bit records rec[n][k] (row pitch ldr, uint16) of the
+ * physical planes, so parity with an implementation of the logical format does not
+ * depend on this library's layout. */
+int w12_unpack_records(const w12_tensor *t, uint16_t *rec, int64_t ldr, hipStream_t stream);
+
+/* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only. */
+int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
+
+/*
+ * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, n < N (summary page method bullet of
+ * section 4.1: the GEMM decodes W12 records in registers and reduces in a fixed order).
+ * X: BF16 [M][ldx]; Y: FP32 [M][ldy], every Y[m][n] (n < N) is written.  Accumulation is
+ * FP32; the result is within 2^-12 * sum_k |x w| of the exact sum and bitwise identical
+ * from run to run on the same device for the same (M, N, K).  M <= 8 runs a wavefront
+ * GEMV, larger M runs bf16 MFMA tiles.  ws: device workspace of at least
+ * w12_gemm_workspace_size bytes (its contents on entry do not matter).
+ */
+int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
+             float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* How w12_gemm will run (M, N, K): path (1 = GEMV, 2 = MFMA), K splits, grid size. */
+typedef struct w12_gemm_plan_info {
+  int32_t path;
+  int32_t splits;
+  int32_t rows_per_block;
+  int32_t m_tile;
+  int64_t grid;
+  uint64_t workspace_bytes;
+} w12_gemm_plan_info;
+int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info *info);
+
+/* Stored bits per weight: (1.5*N*K + N + 4*(N+1) + 4*E) * 8 / (N*K). */
+double w12_bits_per_weight(int32_t N, int32_t K, int64_t E);
+
+const char *w12_status_string(int status);
+const char *w12_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W12_H */

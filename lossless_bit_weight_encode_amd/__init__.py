@@ -1,0 +1,25 @@
+"""W12 on MI355X: lossless 12-bit BF16 weights and the decode-in-register skinny GEMM.
+
+The compute lives in libw12.so (hand-written HIP for gfx950, C ABI in include/w12.h);
+this package only marshals arguments to it.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    W12Error,
+    W12Tensor,
+    alloc_planes,
+    bits_per_weight,
+    decode,
+    encode,
+    encode_count,
+    encode_emit,
+    gemm,
+    gemm_plan,
+    gemm_workspace_size,
+    layout_bytes,
+    lib,
+    unpack_records,
+    verify,
+    verify_async,
+)

@@ -1,0 +1,260 @@
+"""ctypes binding of libw12.so: argument marshalling only.
+
+Every step of encode / decode / verify / GEMM runs in the HIP kernels of libw12.so.
+PyTorch provides device memory and the current stream.  If the library is not built, or
+a tensor is not on a GPU, the calls raise: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw12.so")
+
+W12_OK = 0
+W12_LAYOUT_RB16_K16 = 1
+
+_c_i32, _c_i64, _c_u64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [
+        ("N", _c_i32), ("K", _c_i32), ("layout", _c_i32), ("reserved", _c_i32),
+        ("num_escapes", _c_i64),
+        ("base", _c_p), ("hi", _c_p), ("lo", _c_p), ("esc_ptr", _c_p), ("esc", _c_p),
+    ]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("path", _c_i32), ("splits", _c_i32), ("rows_per_block", _c_i32), ("m_tile", _c_i32),
+        ("grid", _c_i64), ("workspace_bytes", _c_u64),
+    ]
+
+
+_SIGNATURES = {
+    "w12_layout_bytes": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_c_u64), ctypes.POINTER(_c_u64)]),
+    "w12_encode_count": (ctypes.c_int, [_c_p, _c_i32, _c_i32, _c_i64, _c_p, _c_p, _c_p, _c_p]),
+    "w12_encode_emit": (ctypes.c_int, [_c_p, _c_i64, ctypes.POINTER(_Tensor), _c_p]),
+    "w12_decode": (ctypes.c_int, [ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p]),
+    "w12_verify": (ctypes.c_int, [ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_p]),
+    "w12_unpack_records": (ctypes.c_int, [ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p]),
+    "w12_gemm_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_u64)]),
+    "w12_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
+    "w12_gemm_plan": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_PlanInfo)]),
+    "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
+    "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "w12_last_error": (ctypes.c_char_p, []),
+}
+
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class W12Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw12.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m lossless_bit_weight_encode_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(handle, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != W12_OK:
+        msg = lib().w12_last_error().decode()
+        raise W12Error(fn, status, msg or lib().w12_status_string(status).decode())
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _pitch(t: torch.Tensor) -> int:
+    """Row pitch in elements.  A single-row matrix is never stepped by its pitch, and torch
+    may report any stride for a size-1 dimension, so it gets its padded width."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride 1 along k)")
+    if t.shape[0] == 1:
+        return (t.shape[1] + 7) // 8 * 8
+    return t.stride(0)
+
+
+def _require_cuda(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (libw12 has no CPU path)")
+
+
+def _bits16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"expected BF16 bit patterns (bfloat16/int16/uint16), got {t.dtype}")
+    return t
+
+
+def layout_bytes(n: int, k: int) -> tuple[int, int]:
+    hi, lo = _c_u64(), _c_u64()
+    _check("w12_layout_bytes", lib().w12_layout_bytes(n, k, ctypes.byref(hi), ctypes.byref(lo)))
+    return hi.value, lo.value
+
+
+@dataclass
+class W12Tensor:
+    """An encoded tensor: the planes and escape list, all on the GPU."""
+    n: int
+    k: int
+    base: torch.Tensor      # uint8 [N]
+    hi: torch.Tensor        # uint8 [layout hi bytes]
+    lo: torch.Tensor        # uint8 [layout lo bytes]
+    esc_ptr: torch.Tensor   # int32 [N+1] (uint32 values)
+    esc: torch.Tensor       # int32 [E]  (uint32 values)
+
+    @property
+    def num_escapes(self) -> int:
+        return int(self.esc.numel())
+
+    def descriptor(self) -> _Tensor:
+        d = _Tensor()
+        d.N, d.K, d.layout, d.reserved = self.n, self.k, W12_LAYOUT_RB16_K16, 0
+        d.num_escapes = self.num_escapes
+        d.base, d.hi, d.lo = _ptr(self.base), _ptr(self.hi), _ptr(self.lo)
+        d.esc_ptr = _ptr(self.esc_ptr)
+        d.esc = _ptr(self.esc) if self.num_escapes else None
+        return d
+
+    def bits_per_weight(self) -> float:
+        return bits_per_weight(self.n, self.k, self.num_escapes)
+
+    def nbytes(self) -> int:
+        """Bytes of the logical format: 1.5 per weight + base + pointers + 4 per escape."""
+        return int(1.5 * self.n * self.k) + self.n + 4 * (self.n + 1) + 4 * self.num_escapes
+
+
+def alloc_planes(n: int, k: int, device) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
+    hib, lob = layout_bytes(n, k)
+    base = torch.empty(n, dtype=torch.uint8, device=device)
+    hi = torch.empty(hib, dtype=torch.uint8, device=device)
+    lo = torch.empty(lob, dtype=torch.uint8, device=device)
+    esc_ptr = torch.empty(n + 1, dtype=torch.int32, device=device)
+    return base, hi, lo, esc_ptr
+
+
+def encode_count(w: torch.Tensor, base: torch.Tensor, esc_ptr: torch.Tensor, forced_base: torch.Tensor | None = None,
+                 stream=None) -> None:
+    _require_cuda(w, base, esc_ptr, forced_base)
+    _bits16(w)
+    n, k = w.shape
+    _check("w12_encode_count", lib().w12_encode_count(_ptr(w), n, k, _pitch(w), _ptr(forced_base), _ptr(base),
+                                                       _ptr(esc_ptr), _stream(stream)))
+
+
+def encode_emit(w: torch.Tensor, t: W12Tensor, stream=None) -> None:
+    _require_cuda(w)
+    _bits16(w)
+    d = t.descriptor()
+    _check("w12_encode_emit", lib().w12_encode_emit(_ptr(w), _pitch(w), ctypes.byref(d), _stream(stream)))
+
+
+def encode(w: torch.Tensor, forced_base: torch.Tensor | None = None, stream=None) -> W12Tensor:
+    """BF16 [N, K] on the GPU -> W12Tensor.  Reads E back once (one synchronisation)."""
+    _require_cuda(w)
+    _bits16(w)
+    n, k = w.shape
+    base, hi, lo, esc_ptr = alloc_planes(n, k, w.device)
+    encode_count(w, base, esc_ptr, forced_base, stream)
+    e = int(esc_ptr[n].item()) & 0xFFFFFFFF
+    esc = torch.empty(e, dtype=torch.int32, device=w.device)
+    t = W12Tensor(n, k, base, hi, lo, esc_ptr, esc)
+    encode_emit(w, t, stream)
+    return t
+
+
+def decode(t: W12Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if out is None:
+        # rows padded to a multiple of 8 elements (the 16-byte store granule), viewed to K
+        ld = (t.k + 7) // 8 * 8
+        out = torch.empty(t.n, ld, dtype=torch.bfloat16, device=t.hi.device)[:, :t.k]
+    _require_cuda(out)
+    d = t.descriptor()
+    _check("w12_decode", lib().w12_decode(ctypes.byref(d), _ptr(out), _pitch(out), _stream(stream)))
+    return out
+
+
+def verify_async(t: W12Tensor, ref: torch.Tensor, result: torch.Tensor, stream=None) -> None:
+    _require_cuda(ref, result)
+    d = t.descriptor()
+    _check("w12_verify", lib().w12_verify(ctypes.byref(d), _ptr(ref), _pitch(ref), _ptr(result), _stream(stream)))
+
+
+def verify(t: W12Tensor, ref: torch.Tensor, stream=None) -> tuple[int, int]:
+    """(mismatch count, first bad flat index or -1); synchronises to read the result."""
+    result = torch.empty(2, dtype=torch.int64, device=ref.device)
+    verify_async(t, ref, result, stream)
+    cnt, first = (int(v) for v in result.cpu().tolist())
+    return cnt, (-1 if first == -1 else first)
+
+
+def unpack_records(t: W12Tensor, stream=None) -> torch.Tensor:
+    rec = torch.empty(t.n, t.k, dtype=torch.int16, device=t.hi.device)
+    d = t.descriptor()
+    _check("w12_unpack_records", lib().w12_unpack_records(ctypes.byref(d), _ptr(rec), _pitch(rec), _stream(stream)))
+    return rec
+
+
+def gemm_workspace_size(m: int, n: int, k: int) -> int:
+    b = _c_u64()
+    _check("w12_gemm_workspace_size", lib().w12_gemm_workspace_size(m, n, k, ctypes.byref(b)))
+    return b.value
+
+
+def gemm_plan(m: int, n: int, k: int) -> dict:
+    info = _PlanInfo()
+    _check("w12_gemm_plan", lib().w12_gemm_plan(m, n, k, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+
+
+def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+         stream=None) -> torch.Tensor:
+    """Y[M, N] (FP32) = X[M, K] (BF16) @ W^T with W12 weights."""
+    _require_cuda(x)
+    _bits16(x)
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty(m, t.n, dtype=torch.float32, device=x.device)
+    need = gemm_workspace_size(m, t.n, t.k)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    d = t.descriptor()
+    _check("w12_gemm", lib().w12_gemm(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
+                                      _stream(stream)))
+    return y
+
+
+def bits_per_weight(n: int, k: int, e: int) -> float:
+    return float(lib().w12_bits_per_weight(n, k, e))

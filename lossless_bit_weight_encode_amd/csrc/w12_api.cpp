@@ -1,0 +1,188 @@
+// C ABI of libw12: argument validation (host only, before any HIP call), planning and
+// launches.  The declarations and their contracts are in include/w12.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "w12_device.h"
+#include "w12_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return W12_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxK = 65536;
+constexpr int32_t kMaxM = 4096;
+
+int check_shape(int64_t N, int64_t K) {
+  if (N < 1 || N > kMaxN) return fail(W12_ERR_UNSUPPORTED_SHAPE, "N=%lld outside 1..%lld", (long long)N, (long long)kMaxN);
+  if (K < 1 || K > kMaxK) return fail(W12_ERR_UNSUPPORTED_SHAPE, "K=%lld outside 1..65536", (long long)K);
+  if (N * K >= (int64_t(1) << 32)) return fail(W12_ERR_UNSUPPORTED_SHAPE, "N*K=%lld must be below 2^32", (long long)(N * K));
+  return W12_OK;
+}
+
+// A BF16 matrix accessed with 16-byte vector loads/stores: aligned base, pitch >= cols and
+// a multiple of 8 elements.
+int check_bf16_matrix(const void* p, int64_t ld, int64_t cols, const char* what) {
+  if (!p) return fail(W12_ERR_INVALID_ARG, "%s is NULL", what);
+  if (ld < cols) return fail(W12_ERR_INVALID_ARG, "%s pitch %lld < %lld columns", what, (long long)ld, (long long)cols);
+  if (!aligned(p, 16)) return fail(W12_ERR_MISALIGNED, "%s must be 16-byte aligned", what);
+  if (ld % 8) return fail(W12_ERR_MISALIGNED, "%s pitch %lld must be a multiple of 8 elements", what, (long long)ld);
+  return W12_OK;
+}
+
+int check_tensor(const w12_tensor* t) {
+  if (!t) return fail(W12_ERR_INVALID_ARG, "tensor descriptor is NULL");
+  int rc = check_shape(t->N, t->K);
+  if (rc) return rc;
+  if (t->layout != W12_LAYOUT_RB16_K16) return fail(W12_ERR_INVALID_ARG, "unknown layout %d", t->layout);
+  if (t->reserved != 0) return fail(W12_ERR_INVALID_ARG, "reserved field must be 0");
+  if (!t->base || !t->hi || !t->lo || !t->esc_ptr) return fail(W12_ERR_INVALID_ARG, "tensor has a NULL plane");
+  if (t->num_escapes < 0 || t->num_escapes > (int64_t)t->N * t->K)
+    return fail(W12_ERR_INVALID_ARG, "num_escapes=%lld outside 0..N*K", (long long)t->num_escapes);
+  if (t->num_escapes > 0 && !t->esc) return fail(W12_ERR_INVALID_ARG, "esc is NULL with num_escapes > 0");
+  if (!aligned(t->hi, 16) || !aligned(t->lo, 16)) return fail(W12_ERR_MISALIGNED, "hi and lo must be 16-byte aligned");
+  if (!aligned(t->esc_ptr, 4) || (t->esc && !aligned(t->esc, 4))) return fail(W12_ERR_MISALIGNED, "esc_ptr/esc must be 4-byte aligned");
+  return W12_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W12_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int w12_layout_bytes(int32_t N, int32_t K, uint64_t* hi_bytes, uint64_t* lo_bytes) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (!hi_bytes || !lo_bytes) return fail(W12_ERR_INVALID_ARG, "output pointer is NULL");
+  const uint64_t chunks = (uint64_t)w12::num_row_blocks(N) * (uint64_t)w12::num_chunks(K);
+  *hi_bytes = chunks * w12::kHiChunkBytes;
+  *lo_bytes = chunks * w12::kLoChunkBytes;
+  return ok();
+}
+
+int w12_encode_count(const uint16_t* W, int32_t N, int32_t K, int64_t ldw, const uint8_t* forced_base,
+                     uint8_t* base, uint32_t* esc_ptr, hipStream_t stream) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if ((rc = check_bf16_matrix(W, ldw, K, "W"))) return rc;
+  if (!base || !esc_ptr) return fail(W12_ERR_INVALID_ARG, "base or esc_ptr is NULL");
+  if (!aligned(esc_ptr, 4)) return fail(W12_ERR_MISALIGNED, "esc_ptr must be 4-byte aligned");
+  return hip_status(w12::launch_encode_count(W, N, K, ldw, forced_base, base, esc_ptr, stream), "encode_count");
+}
+
+int w12_encode_emit(const uint16_t* W, int64_t ldw, const w12_tensor* t, hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if ((rc = check_bf16_matrix(W, ldw, t->K, "W"))) return rc;
+  return hip_status(w12::launch_encode_emit(W, ldw, t, stream), "encode_emit");
+}
+
+int w12_decode(const w12_tensor* t, uint16_t* out, int64_t ldo, hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if ((rc = check_bf16_matrix(out, ldo, t->K, "out"))) return rc;
+  return hip_status(w12::launch_decode(t, out, ldo, stream), "decode");
+}
+
+int w12_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, unsigned long long* d_result,
+               hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if ((rc = check_bf16_matrix(ref, ldr, t->K, "ref"))) return rc;
+  if (!d_result) return fail(W12_ERR_INVALID_ARG, "d_result is NULL");
+  if (!aligned(d_result, 8)) return fail(W12_ERR_MISALIGNED, "d_result must be 8-byte aligned");
+  return hip_status(w12::launch_verify(t, ref, ldr, d_result, stream), "verify");
+}
+
+int w12_unpack_records(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if (!rec) return fail(W12_ERR_INVALID_ARG, "rec is NULL");
+  if (ldr < t->K) return fail(W12_ERR_INVALID_ARG, "rec pitch %lld < K", (long long)ldr);
+  if (!aligned(rec, 2)) return fail(W12_ERR_MISALIGNED, "rec must be 2-byte aligned");
+  return hip_status(w12::launch_unpack(t, rec, ldr, stream), "unpack_records");
+}
+
+int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t* bytes) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
+  if (!bytes) return fail(W12_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = w12::plan_gemm(M, N, K).ws_bytes;
+  return ok();
+}
+
+int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info* info) {
+  int rc = check_shape(N, K);
+  if (rc) return rc;
+  if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
+  if (!info) return fail(W12_ERR_INVALID_ARG, "info is NULL");
+  const w12::GemmPlan p = w12::plan_gemm(M, N, K);
+  info->path = p.path;
+  info->splits = p.splits;
+  info->rows_per_block = p.rb * w12::kRowsPerBlock;
+  info->m_tile = p.m_tile;
+  info->grid = p.grid;
+  info->workspace_bytes = p.ws_bytes;
+  return ok();
+}
+
+int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
+             uint64_t ws_bytes, hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
+  if ((rc = check_bf16_matrix(X, ldx, t->K, "X"))) return rc;
+  if (!Y) return fail(W12_ERR_INVALID_ARG, "Y is NULL");
+  if (ldy < t->N) return fail(W12_ERR_INVALID_ARG, "Y pitch %lld < N", (long long)ldy);
+  if (!aligned(Y, 4)) return fail(W12_ERR_MISALIGNED, "Y must be 4-byte aligned");
+  const w12::GemmPlan p = w12::plan_gemm(M, t->N, t->K);
+  if (ws_bytes < p.ws_bytes)
+    return fail(W12_ERR_WORKSPACE_TOO_SMALL, "workspace %llu bytes < %llu needed", (unsigned long long)ws_bytes,
+                (unsigned long long)p.ws_bytes);
+  if (p.ws_bytes && !ws) return fail(W12_ERR_INVALID_ARG, "ws is NULL");
+  if (ws && !aligned(ws, 16)) return fail(W12_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  return hip_status(w12::launch_gemm(p, X, M, ldx, t, Y, ldy, ws, stream), "gemm");
+}
+
+double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {
+  if (N < 1 || K < 1 || E < 0) return -1.0;
+  const double nk = (double)N * (double)K;
+  return (1.5 * nk + (double)N + 4.0 * ((double)N + 1.0) + 4.0 * (double)E) * 8.0 / nk;
+}
+
+const char* w12_status_string(int status) {
+  switch (status) {
+    case W12_OK: return "ok";
+    case W12_ERR_INVALID_ARG: return "invalid argument";
+    case W12_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case W12_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case W12_ERR_HIP: return "HIP error";
+    case W12_ERR_MISALIGNED: return "misaligned pointer or pitch";
+    default: return "unknown status";
+  }
+}
+
+const char* w12_last_error(void) { return g_err; }
+
+}  // extern "C"

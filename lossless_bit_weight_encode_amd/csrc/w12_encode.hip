@@ -1,0 +1,215 @@
+// W12 encode kernels: per-channel window choice, escape-count scan, record emission.
+//
+// SpecPilot summary page, method bullet of section 4.1: each weight becomes sign | 4-bit
+// exponent offset inside a 16-binade window per output channel | 7 mantissa bits, and
+// out-of-window weights, zeros and denormals go to an exact escape list.  News article
+// "(1) W12": BF16 exponents cluster within an output channel, which is what makes a
+// per-channel window pay.  The window base b of a channel is the smallest b in 1..239 that
+// maximises the number of weights with exponent field in [b, b+15].
+#include "w12_device.h"
+#include "w12_kernels.h"
+
+namespace w12 {
+
+constexpr int kCountWaves = 4;
+
+// One wave per channel: LDS exponent histogram, then the best 16-wide window.
+__global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
+    const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, const uint8_t* __restrict__ forced,
+    uint8_t* __restrict__ base, uint32_t* __restrict__ esc_ptr) {
+  __shared__ uint32_t hist[kCountWaves][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * kCountWaves + wave;
+  uint32_t* h = hist[wave];
+  for (int i = lane; i < 256; i += kWave) h[i] = 0;
+  __syncthreads();
+  if (n < N) {
+    const uint16_t* row = W + n * ldw;
+    for (int k = lane * 8; k < K; k += kWave * 8) {
+      uint32_t v[4];
+      if (k + 8 <= K) {
+        const uint4 q = *reinterpret_cast<const uint4*>(row + k);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          atomicAdd(&h[(v[i] >> 7) & 0xFFu], 1u);
+          atomicAdd(&h[(v[i] >> 23) & 0xFFu], 1u);
+        }
+      } else {
+        for (int i = k; i < K; ++i) atomicAdd(&h[(row[i] >> 7) & 0xFFu], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (n < N) {
+    uint32_t best;
+    if (forced) {
+      uint32_t b = forced[n];
+      b = b < 1u ? 1u : (b > 239u ? 239u : b);
+      uint32_t c = 0;
+      for (uint32_t e = b; e < b + 16; ++e) c += h[e];
+      best = (c << 8) | (255u - b);
+    } else {
+      // key = count << 8 | (255 - b): the max key has the largest count and, among equal
+      // counts, the smallest b.
+      best = 0;
+      for (int b = lane + 1; b <= 239; b += kWave) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c += h[b + e];
+        const uint32_t key = (c << 8) | (255u - (uint32_t)b);
+        best = key > best ? key : best;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t o = __shfl_xor(best, off, kWave);
+        best = o > best ? o : best;
+      }
+    }
+    if (lane == 0) {
+      base[n] = (uint8_t)(255u - (best & 0xFFu));
+      esc_ptr[n + 1] = (uint32_t)K - (best >> 8);
+    }
+  }
+}
+
+// esc_ptr[0] = 0 and an inclusive scan of the counts in esc_ptr[1..N] (one work-group).
+__global__ __launch_bounds__(1024) void k_scan_counts(uint32_t* __restrict__ esc_ptr, int32_t N) {
+  __shared__ uint32_t part[1024];
+  const int t = threadIdx.x;
+  const int64_t per = ((int64_t)N + 1023) / 1024;
+  const int64_t lo = 1 + (int64_t)t * per;
+  const int64_t hi = (lo + per < (int64_t)N + 1) ? lo + per : (int64_t)N + 1;
+  uint32_t s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += esc_ptr[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = (t >= off) ? part[t - off] : 0u;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  uint32_t run = (t > 0) ? part[t - 1] : 0u;
+  for (int64_t i = lo; i < hi; ++i) {
+    run += esc_ptr[i];
+    esc_ptr[i] = run;
+  }
+  if (t == 0) esc_ptr[0] = 0;
+}
+
+constexpr int kEmitWaves = 4;
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// One wave per (padded) row; lane l owns chunk c0 + l (16 consecutive k).  Records go to the
+// hi/lo planes; escapes are compacted in ascending k: every lane counts its escapes, a
+// wavefront prefix sum (one ballot per bit of the count) gives its slot after the channel's
+// running offset.
+__global__ __launch_bounds__(kEmitWaves * kWave) void k_encode_emit(
+    const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, int64_t Np, int64_t Kc,
+    const uint8_t* __restrict__ base, const uint32_t* __restrict__ esc_ptr, uint8_t* __restrict__ hi,
+    uint8_t* __restrict__ lo, uint32_t* __restrict__ esc, uint32_t num_esc) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * kEmitWaves + wave;
+  if (n >= Np) return;
+  const bool real = n < N;
+  const int64_t rb = n / kRowsPerBlock;
+  const int r = (int)(n % kRowsPerBlock);
+  const uint32_t b = real ? base[n] : 1u;
+  uint32_t slot = real ? esc_ptr[n] : 0u;
+  const uint16_t* row = W + (real ? n : 0) * ldw;
+  for (int64_t c0 = 0; c0 < Kc; c0 += kWave) {
+    const int64_t c = c0 + lane;
+    const bool active = c < Kc;
+    uint32_t v[16];
+    int valid = 0;
+    if (active && real) {
+      const int64_t rem = (int64_t)K - c * kChunkK;
+      valid = rem >= kChunkK ? kChunkK : (int)rem;
+      uint4 a, bq;
+      load16_bf16(row + c * kChunkK, valid, a, bq);
+      const uint32_t w2[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = w2[i] & 0xFFFFu;
+        v[2 * i + 1] = w2[i] >> 16;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 0;
+    }
+    uint32_t rec[16];
+    uint32_t escmask = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t e = (v[j] >> 7) & 0xFFu;
+      const bool in = (e >= b) && (e <= b + 15u);
+      const bool isreal = j < valid;
+      rec[j] = (in && isreal) ? (((v[j] >> 15) << 11) | ((e - b) << 7) | (v[j] & 0x7Fu)) : 0u;
+      if (isreal && !in) escmask |= 1u << j;
+    }
+    if (active) {
+      uint32_t hw[4], lw[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hw[i] = (rec[4 * i] >> 4) | ((rec[4 * i + 1] >> 4) << 8) | ((rec[4 * i + 2] >> 4) << 16) |
+                ((rec[4 * i + 3] >> 4) << 24);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t byte = ((rec[8 * d + i] & 0xFu) << 4) | (rec[8 * d + 4 + i] & 0xFu);
+          x |= byte << (8 * i);
+        }
+        lw[d] = x;
+      }
+      *reinterpret_cast<uint4*>(hi + hi_offset(rb, c, Kc, r)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint2*>(lo + lo_offset(rb, c, Kc, r)) = make_uint2(lw[0], lw[1]);
+    }
+    if (real) {
+      const uint32_t cnt = __builtin_popcount(escmask);
+      uint32_t prefix = 0, total = 0;
+#pragma unroll
+      for (int bit = 0; bit < 5; ++bit) {
+        const uint64_t m = __ballot((cnt >> bit) & 1u);
+        prefix += lanes_below(m) << bit;
+        total += (uint32_t)__popcll(m) << bit;
+      }
+      uint32_t o = slot + prefix;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (escmask & (1u << j)) {
+          if (o < num_esc) esc[o] = ((uint32_t)(c * kChunkK + j) << 16) | v[j];
+          ++o;
+        }
+      }
+      slot += total;
+    }
+  }
+}
+
+hipError_t launch_encode_count(const uint16_t* W, int32_t N, int32_t K, int64_t ldw, const uint8_t* forced,
+                               uint8_t* base, uint32_t* esc_ptr, hipStream_t stream) {
+  const unsigned grid = (unsigned)((N + kCountWaves - 1) / kCountWaves);
+  hipLaunchKernelGGL(k_encode_count, dim3(grid), dim3(kCountWaves * kWave), 0, stream, W, N, K, ldw, forced, base,
+                     esc_ptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, stream, esc_ptr, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_emit(const uint16_t* W, int64_t ldw, const w12_tensor* t, hipStream_t stream) {
+  const int64_t Np = num_row_blocks(t->N) * kRowsPerBlock;
+  const int64_t Kc = num_chunks(t->K);
+  const unsigned grid = (unsigned)((Np + kEmitWaves - 1) / kEmitWaves);
+  hipLaunchKernelGGL(k_encode_emit, dim3(grid), dim3(kEmitWaves * kWave), 0, stream, W, t->N, t->K, ldw, Np, Kc,
+                     t->base, t->esc_ptr, t->hi, t->lo, t->esc, (uint32_t)t->num_escapes);
+  return hipGetLastError();
+}
+
+}  // namespace w12

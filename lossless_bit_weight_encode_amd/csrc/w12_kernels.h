@@ -1,0 +1,37 @@
+// Internal launch helpers of libw12 (host side).  Arguments are validated by the C ABI
+// layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w12.h"
+
+namespace w12 {
+
+hipError_t launch_encode_count(const uint16_t* W, int32_t N, int32_t K, int64_t ldw, const uint8_t* forced,
+                               uint8_t* base, uint32_t* esc_ptr, hipStream_t stream);
+hipError_t launch_encode_emit(const uint16_t* W, int64_t ldw, const w12_tensor* t, hipStream_t stream);
+
+hipError_t launch_decode(const w12_tensor* t, uint16_t* out, int64_t ldo, hipStream_t stream);
+hipError_t launch_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, unsigned long long* d_result,
+                         hipStream_t stream);
+hipError_t launch_unpack(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStream_t stream);
+
+struct GemmPlan {
+  int path;            // 1 = GEMV (M <= 8), 2 = MFMA
+  int splits;          // K splits across work-groups (S)
+  int rb;              // row blocks of 16 per work-group
+  int waves;           // waves per work-group (they split the work-group's K range)
+  int m_tile;          // rows of X per work-group (MFMA path)
+  int m_tiles;         // number of m tiles
+  int64_t row_groups;  // ceil(Nb / rb)
+  int64_t grid;        // row_groups * splits * m_tiles
+  uint64_t ws_bytes;   // split-K partials
+};
+
+GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K);
+hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
+                       int64_t ldy, void* ws, hipStream_t stream);
+
+}  // namespace w12

