@@ -125,8 +125,16 @@ int w12_verify(const w12_tensor *t, const uint16_t *ref, int64_t ldr,
  * depend on this library's layout. */
 int w12_unpack_records(const w12_tensor *t, uint16_t *rec, int64_t ldr, hipStream_t stream);
 
-/* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only. */
+/* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only.
+ * The workspace starts with one 32-bit arrival counter per output tile (split-K
+ * bookkeeping) followed by the FP32 slice partials. */
 int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
+
+/* Zero-fill a GEMM workspace of ws_bytes bytes on `stream`.  Call it once after allocating
+ * the workspace: w12_gemm needs the counter region to be zero on entry and leaves it zero
+ * when it completes, so the workspace can then serve any sequence of w12_gemm calls on one
+ * stream.  Calls that overlap in time on one workspace race. */
+int w12_gemm_workspace_init(void *ws, uint64_t ws_bytes, hipStream_t stream);
 
 /*
  * Y[m][n] = sum_k X[m][k] * W[n][k] for m < M, n < N (summary page method bullet of
@@ -134,20 +142,24 @@ int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
  * X: BF16 [M][ldx]; Y: FP32 [M][ldy], every Y[m][n] (n < N) is written.  Accumulation is
  * FP32; the result is within 2^-12 * sum_k |x w| of the exact sum and bitwise identical
  * from run to run on the same device for the same (M, N, K).  M <= 8 runs a wavefront
- * GEMV, larger M runs bf16 MFMA tiles.  ws: device workspace of at least
- * w12_gemm_workspace_size bytes (its contents on entry do not matter).
+ * GEMV, larger M runs bf16 MFMA tiles.  The K range may be split over several work-groups;
+ * the last one to finish a tile sums the slice partials in increasing slice order (no
+ * floating-point atomics).  ws: device workspace of at least w12_gemm_workspace_size bytes,
+ * initialised once with w12_gemm_workspace_init (only its counter region must be zero; the
+ * partial region may hold anything on entry).
  */
 int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
              float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
 
-/* How w12_gemm will run (M, N, K): path (1 = GEMV, 2 = MFMA), K splits, grid size. */
+/* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
-  int32_t path;
-  int32_t splits;
-  int32_t rows_per_block;
-  int32_t m_tile;
-  int64_t grid;
-  uint64_t workspace_bytes;
+  int32_t path;              /* 1 = GEMV (M <= 8), 2 = MFMA                              */
+  int32_t splits;            /* K slices per output tile                                 */
+  int32_t rows_per_block;    /* rows of W per work-group tile                            */
+  int32_t m_tile;            /* rows of X per work-group tile                            */
+  int64_t grid;              /* work-groups launched                                     */
+  uint64_t workspace_bytes;  /* == w12_gemm_workspace_size                               */
+  uint64_t counter_bytes;    /* leading bytes of the workspace holding arrival counters */
 } w12_gemm_plan_info;
 int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info *info);
 

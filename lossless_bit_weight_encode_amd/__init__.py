@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     encode_emit,
     gemm,
     gemm_plan,
+    gemm_workspace,
+    gemm_workspace_init,
     gemm_workspace_size,
     layout_bytes,
     lib,

@@ -32,7 +32,7 @@ class _Tensor(ctypes.Structure):
 class _PlanInfo(ctypes.Structure):
     _fields_ = [
         ("path", _c_i32), ("splits", _c_i32), ("rows_per_block", _c_i32), ("m_tile", _c_i32),
-        ("grid", _c_i64), ("workspace_bytes", _c_u64),
+        ("grid", _c_i64), ("workspace_bytes", _c_u64), ("counter_bytes", _c_u64),
     ]
 
 
@@ -44,6 +44,7 @@ _SIGNATURES = {
     "w12_verify": (ctypes.c_int, [ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_p]),
     "w12_unpack_records": (ctypes.c_int, [ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p]),
     "w12_gemm_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_u64)]),
+    "w12_gemm_workspace_init": (ctypes.c_int, [_c_p, _c_u64, _c_p]),
     "w12_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
     "w12_gemm_plan": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_PlanInfo)]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
@@ -238,17 +239,35 @@ def gemm_plan(m: int, n: int, k: int) -> dict:
     return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
 
 
+def gemm_workspace_init(ws: torch.Tensor, stream=None) -> None:
+    _require_cuda(ws)
+    _check("w12_gemm_workspace_init",
+           lib().w12_gemm_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gemm_workspace(m: int, n: int, k: int, device="cuda", stream=None) -> torch.Tensor | None:
+    """A ready-to-use (zero-initialised) workspace for gemm() with M=m on W[n][k], or None."""
+    need = gemm_workspace_size(m, n, k)
+    if not need:
+        return None
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    gemm_workspace_init(ws, stream)
+    return ws
+
+
 def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
          stream=None) -> torch.Tensor:
-    """Y[M, N] (FP32) = X[M, K] (BF16) @ W^T with W12 weights."""
+    """Y[M, N] (FP32) = X[M, K] (BF16) @ W^T with W12 weights.
+
+    ws: a workspace from gemm_workspace() (or any buffer of at least gemm_workspace_size bytes
+    initialised once with gemm_workspace_init); one is allocated here when omitted."""
     _require_cuda(x)
     _bits16(x)
     m = x.shape[0]
     if y is None:
         y = torch.empty(m, t.n, dtype=torch.float32, device=x.device)
-    need = gemm_workspace_size(m, t.n, t.k)
-    if ws is None and need:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if ws is None:
+        ws = gemm_workspace(m, t.n, t.k, x.device, stream)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     d = t.descriptor()
     _check("w12_gemm", lib().w12_gemm(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,

@@ -33,6 +33,9 @@ int check_shape(int64_t N, int64_t K) {
   if (N < 1 || N > kMaxN) return fail(W12_ERR_UNSUPPORTED_SHAPE, "N=%lld outside 1..%lld", (long long)N, (long long)kMaxN);
   if (K < 1 || K > kMaxK) return fail(W12_ERR_UNSUPPORTED_SHAPE, "K=%lld outside 1..65536", (long long)K);
   if (N * K >= (int64_t(1) << 32)) return fail(W12_ERR_UNSUPPORTED_SHAPE, "N*K=%lld must be below 2^32", (long long)(N * K));
+  // the GEMM addresses the hi plane with 32-bit buffer offsets
+  if (w12::num_row_blocks(N) * w12::num_chunks(K) * w12::kHiChunkBytes >= (int64_t(1) << 32))
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "padded N x K too large for 32-bit plane offsets");
   return W12_OK;
 }
 
@@ -144,7 +147,15 @@ int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info* info) {
   info->m_tile = p.m_tile;
   info->grid = p.grid;
   info->workspace_bytes = p.ws_bytes;
+  info->counter_bytes = p.counter_bytes;
   return ok();
+}
+
+int w12_gemm_workspace_init(void* ws, uint64_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes == 0) return ok();
+  if (!ws) return fail(W12_ERR_INVALID_ARG, "ws is NULL");
+  if (!aligned(ws, 16)) return fail(W12_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  return hip_status(w12::init_gemm_workspace(ws, ws_bytes, stream), "gemm_workspace_init");
 }
 
 int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
@@ -153,6 +164,8 @@ int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, flo
   if (rc) return rc;
   if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
   if ((rc = check_bf16_matrix(X, ldx, t->K, "X"))) return rc;
+  if (((int64_t)M - 1) * ldx + t->K + 16 >= (int64_t(1) << 30))
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "X spans too many elements for 31-bit buffer offsets");
   if (!Y) return fail(W12_ERR_INVALID_ARG, "Y is NULL");
   if (ldy < t->N) return fail(W12_ERR_INVALID_ARG, "Y pitch %lld < N", (long long)ldy);
   if (!aligned(Y, 4)) return fail(W12_ERR_MISALIGNED, "Y must be 4-byte aligned");

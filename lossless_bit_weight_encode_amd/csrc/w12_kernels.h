@@ -20,17 +20,24 @@ hipError_t launch_unpack(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStr
 
 struct GemmPlan {
   int path;            // 1 = GEMV (M <= 8), 2 = MFMA
-  int splits;          // K splits across work-groups (S)
-  int rb;              // row blocks of 16 per work-group
-  int waves;           // waves per work-group (they split the work-group's K range)
-  int m_tile;          // rows of X per work-group (MFMA path)
+  int splits;          // work-group segments per tile (1 when work-groups cover whole tiles)
+  int rb;              // row blocks of 16 per tile
+  int waves;           // waves per work-group (they split a segment's K range)
+  int m_tile;          // rows of X per tile
   int m_tiles;         // number of m tiles
   int64_t row_groups;  // ceil(Nb / rb)
-  int64_t grid;        // row_groups * splits * m_tiles
-  uint64_t ws_bytes;   // split-K partials
+  int64_t tiles;       // row_groups * m_tiles
+  int64_t upt;         // stream-K units (16 chunks) per tile
+  int64_t units;       // tiles * upt
+  int64_t grid;        // work-groups G (resident at once; each takes units / G units)
+  uint64_t counter_bytes;  // per-tile arrival counters at the start of the workspace
+  uint64_t partial_bytes;  // two partial tiles per work-group
+  uint64_t xpad_bytes;     // X padded to whole 16-k chunks (only when K % 16 != 0)
+  uint64_t ws_bytes;       // counters + partials + padded X
 };
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K);
+hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream);
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, hipStream_t stream);
 

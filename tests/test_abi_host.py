@@ -121,8 +121,12 @@ def test_gemm_plan_is_consistent(m, n, k):
     assert p["path"] == (1 if m <= 8 else 2)
     assert p["splits"] >= 1
     kc = (k + 15) // 16
-    # every lane sub-range holds at least one chunk unless the whole K is tiny
-    if p["splits"] > 1:
-        assert kc // (16 * p["splits"]) >= 1
-    assert p["workspace_bytes"] == (0 if p["splits"] == 1 else p["splits"] * m * n * 4)
+    upt = (kc + 15) // 16                       # stream-K units (16 chunks) per tile
+    tiles = ((n + 15) // 16 + 3) // 4 * ((m + p["m_tile"] - 1) // p["m_tile"])
+    assert 1 <= p["grid"] <= tiles * upt       # never more work-groups than units
+    assert p["counter_bytes"] % 256 == 0 and p["counter_bytes"] >= 4 * tiles
+    # counters + two partial tiles (64 rows x m tile) per work-group (+ X padded to whole
+    # 16-k chunks when K is ragged)
+    xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
+    assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * 64 * p["m_tile"] * 4 + xpad
     assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]

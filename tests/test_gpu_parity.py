@@ -172,18 +172,40 @@ def test_gemm_within_tolerance(name, m):
 
 @pytest.mark.parametrize("m", [1, 4, 8, 16, 32, 64, 100])
 def test_gemm_bitwise_deterministic(m):
+    """20 runs bitwise identical; the partial region of the workspace is NaN-poisoned before
+    every run so a read of a partial that was never written would show."""
     w, _ = case("gauss_300x4096")
     n, k = w.shape
     t = w12.encode(dev_weights(w))
     x = to_dev(S.activations(m, k, 77 + m))
-    need = w12.gemm_workspace_size(m, n, k)
-    assert w12.gemm_plan(m, n, k)["splits"] > 1, "the determinism test must exercise split-K"
+    plan = w12.gemm_plan(m, n, k)
+    assert plan["splits"] > 1, "the determinism test must exercise split-K"
+    ws = w12.gemm_workspace(m, n, k)
+    cb = plan["counter_bytes"]
     outs = []
     for i in range(20):
-        ws = torch.full((max(need, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
-        outs.append(w12.gemm(x, t, ws=ws.view(torch.uint8)).cpu().numpy().view(np.uint32))
+        ws[cb:].view(torch.float32).fill_(float("nan"))
+        outs.append(w12.gemm(x, t, ws=ws).cpu().numpy().view(np.uint32))
+        assert (ws[:cb].cpu().numpy() == 0).all(), "arrival counters must return to zero"
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+    bad, _ = O.gemm_check(S.activations(m, k, 77 + m), w, outs[0].view(np.float32))
+    assert bad == 0
+
+
+def test_gemm_workspace_reused_across_shapes():
+    """One workspace, sized for the largest call, serves calls of different shapes in turn."""
+    w, _ = case("gauss_300x4096")
+    n, k = w.shape
+    t = w12.encode(dev_weights(w))
+    need = max(w12.gemm_workspace_size(m, n, k) for m in (1, 16, 100))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    w12.gemm_workspace_init(ws)
+    for m in (16, 1, 100, 16, 3):
+        x = S.activations(m, k, 300 + m)
+        y = w12.gemm(to_dev(x), t, ws=ws).cpu().numpy()
+        bad, _ = O.gemm_check(x, w, y)
+        assert bad == 0
 
 
 @pytest.mark.parametrize("m", [3, 24])
