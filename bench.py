@@ -1,0 +1,385 @@
+"""Benchmark of the W12 hot path on one MI355X.
+
+Step = one exact verification pass over one 27B-class dense decoder layer (hidden 5120):
+the four W12 GEMMs qkv [7168x5120], o_proj [5120x5120], gate_up [34816x5120] and
+down [5120x17408] against X [16 rows] (a 16-position drafted block).  Inputs are synthetic
+(seeded Gaussian x per-channel lognormal weights, see w12_synth) and resident in HBM before
+the timed region.  Three encoded copies of the layer (1.49 GB of W12) are rotated so the
+256 MB Infinity Cache cannot serve repeated weight reads.
+
+value = weight-GB/s = BF16-equivalent weight bytes (2*N*K per matrix) per second over the
+timed steps.  Extra legs (same JSON line): the tree-verify M sweep, per-launch roofline of
+the dominant kernel (gate_up), load-time encode/verify throughput, and the CPU oracle
+timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lossless_bit_weight_encode_amd as w12  # noqa: E402
+import w12_synth as S  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(n, k, m, e):
+    """Algorithmic bytes of one GEMM: records, bases, pointers, escapes, X and Y."""
+    return 1.5 * n * k + n + 4 * (n + 1) + 4 * e + 2 * m * k + 4 * m * n
+
+
+def dev_bits(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def clone_tensor(t: w12.W12Tensor) -> w12.W12Tensor:
+    return w12.W12Tensor(t.n, t.k, t.base.clone(), t.hi.clone(), t.lo.clone(), t.esc_ptr.clone(), t.esc.clone())
+
+
+def timed(fn, iters, stream):
+    """Average milliseconds per call of fn over iters calls, HIP events on `stream`."""
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only-layer", action="store_true", help="time only the layer steps (for profiling)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the layer steps, run one torch elementwise kernel that reads and writes exactly "
+                         "256 MiB (the plain kernel of known size against which HBM byte counters are scaled)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of --only-layer into the kernel-time "
+                         "summary under profiles/ (COMMAND is the profiled command line, recorded verbatim)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run of "
+                         "--only-layer --copy-probe) into the per-launch traffic summary under profiles/")
+    args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the W12 path is built and timed on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    m_step = 16
+
+    # ---- inputs (synthetic, seeded; host-generated so bits do not depend on the GPU) ----
+    t0 = time.time()
+    layer = S.layer(0)
+    log(f"[bench] generated layer 0 in {time.time() - t0:.1f}s")
+    names = list(S.LAYER_ORDER)
+    w_dev = {nm: dev_bits(layer[nm]) for nm in names}
+    x_dev = {}
+    for nm in names:
+        n, k = S.LAYER_SHAPES[nm]
+        x_dev[(nm, m_step)] = dev_bits(S.activations(m_step, k, S.x_seed(m_step, k)))
+
+    # ---- load-time leg: encode + verify per matrix ----
+    enc, load_leg = {}, {}
+    for nm in names:
+        w = w_dev[nm]
+        n, k = w.shape
+        t_enc = timed(lambda i: w12.encode(w), 3, stream)
+        enc[nm] = w12.encode(w)
+        res = torch.empty(2, dtype=torch.int64, device=dev)
+        t_ver = timed(lambda i: w12.verify_async(enc[nm], w, res), 5, stream)
+        cnt, first = res.cpu().tolist()
+        assert cnt == 0, f"load-time check failed on {nm}: {cnt} mismatches (first {first})"
+        load_leg[nm] = {
+            "encode_ms": round(t_enc, 4), "encode_GBps": round(2 * n * k / t_enc / 1e6, 1),
+            "verify_ms": round(t_ver, 4),
+            "verify_GBps": round((3.5 * n * k + 5 * n + 4 * enc[nm].num_escapes) / t_ver / 1e6, 1),
+            "escapes": enc[nm].num_escapes, "bits_per_weight": round(enc[nm].bits_per_weight(), 5),
+        }
+        log(f"[bench] {nm}: E={enc[nm].num_escapes} bpw={enc[nm].bits_per_weight():.4f} "
+            f"encode {t_enc:.3f} ms verify {t_ver:.3f} ms")
+    del w_dev
+    torch.cuda.empty_cache()
+
+    copies = [enc] + [{nm: clone_tensor(enc[nm]) for nm in names} for _ in range(args.copies - 1)]
+    y_dev = {nm: torch.empty(m_step, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names}
+    ws = {nm: w12.gemm_workspace(m_step, *S.LAYER_SHAPES[nm]) for nm in names}
+
+    # HIP events bracket every gate_up launch of the timed steps (same stream as the launch);
+    # the host enqueues a step in well under the step's GPU time, so the stream is never idle
+    # between an event and its kernel.
+    ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+    rec = {"on": False}
+
+    def layer_step(i):
+        c = copies[i % len(copies)]
+        for nm in names:
+            if rec["on"] and nm == "gate_up":
+                ev_pairs[i][0].record(stream)
+                w12.gemm(x_dev[(nm, m_step)], c[nm], y=y_dev[nm], ws=ws[nm], stream=stream)
+                ev_pairs[i][1].record(stream)
+            else:
+                w12.gemm(x_dev[(nm, m_step)], c[nm], y=y_dev[nm], ws=ws[nm], stream=stream)
+
+    for i in range(args.warmup):
+        layer_step(i)
+    torch.cuda.synchronize()
+    rec["on"] = True
+    t_step = timed(layer_step, args.steps, stream)
+    rec["on"] = False
+    gate_us = [a.elapsed_time(b) * 1e3 for a, b in ev_pairs]
+    weight_bytes = sum(2 * n * k for n, k in (S.LAYER_SHAPES[nm] for nm in names))
+    moved = sum(alg_bytes(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes) for nm in names)
+    value = weight_bytes / t_step / 1e6
+    log(f"[bench] layer step {t_step * 1e3:.1f} us -> {value:.1f} weight-GB/s, "
+        f"{moved / t_step / 1e6:.1f} GB/s moved")
+
+    out = {
+        "metric": "w12_gemm weight-GB/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "one 27B-class dense decoder layer (hidden 5120): qkv 7168x5120, o_proj 5120x5120, "
+                        "gate_up 34816x5120, down 5120x17408; W12 weights, M=16 BF16 verify rows",
+            "M": m_step,
+            "weights_bf16_bytes": weight_bytes,
+            "bytes_moved_per_step": int(moved),
+            "bytes_moved_GBps": round(moved / t_step / 1e6, 1),
+            "bytes_moved_frac_of_8TBps": round(moved / t_step / 1e6 / HBM_PEAK_GBPS, 4),
+            "rotated_copies": len(copies),
+        },
+    }
+    if args.only_layer:
+        if args.copy_probe:
+            a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            torch.cuda.synchronize()
+            torch.bitwise_not(a, out=b)   # one elementwise kernel: reads and writes 256 MiB
+            torch.cuda.synchronize()
+        print(json.dumps(out))
+        return
+
+    # ---- roofline of the dominant kernel: the gate_up GEMM launch, from the timed steps ----
+    nm = "gate_up"
+    n, k = S.LAYER_SHAPES[nm]
+    t_g = float(np.mean(gate_us)) / 1e3   # ms
+    ab = alg_bytes(n, k, m_step, enc[nm].num_escapes)
+    plan = w12.gemm_plan(m_step, n, k)
+    out["roofline"] = {
+        "bound": "hbm", "achieved": round(ab / t_g / 1e6, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+        "frac": round(ab / t_g / 1e6 / HBM_PEAK_GBPS, 4), "traffic": None,
+        "kernel": kernel_name(plan, m_step),
+        "launch": f"gate_up {n}x{k} M={m_step}, grid={plan['grid']}, segments/tile<={plan['splits']}",
+        "avg_launch_us": round(t_g * 1e3, 2), "median_launch_us": round(float(np.median(gate_us)), 2),
+        "alg_bytes_per_launch": int(ab),
+    }
+    out["roofline"].update(traffic_from_profile(ab))
+    out["load_time"] = load_leg
+
+    # ---- tree-verify M sweep on gate_up and down ----
+    if not args.no_sweep:
+        sweep = {}
+        for nm in ("gate_up", "down"):
+            n, k = S.LAYER_SHAPES[nm]
+            for m in S.TREE_M_SWEEP + (16,):
+                x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
+                y = torch.empty(m, n, dtype=torch.float32, device=dev)
+                wsm = w12.gemm_workspace(m, n, k)
+                for i in range(3):
+                    w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm)
+                t = timed(lambda i: w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm), 30, stream)
+                ab = alg_bytes(n, k, m, enc[nm].num_escapes)
+                sweep[f"{nm}_M{m}"] = {
+                    "us": round(t * 1e3, 2), "weight_GBps": round(2 * n * k / t / 1e6, 1),
+                    "moved_GBps": round(ab / t / 1e6, 1), "frac": round(ab / t / 1e6 / HBM_PEAK_GBPS, 4),
+                    "splits": w12.gemm_plan(m, n, k)["splits"],
+                }
+                log(f"[bench] {nm} M={m}: {t * 1e3:.1f} us, {ab / t / 1e6:.0f} GB/s moved")
+        out["tree_sweep"] = sweep
+
+    # ---- practical HBM ceilings measured with plain torch kernels (context for frac) ----
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    bcp = torch.empty_like(a)
+    t_cp = timed(lambda i: bcp.copy_(a), 10, stream)
+    out["hbm_reference"] = {"copy_1GiB_GBps": round(2 * a.numel() / t_cp / 1e6, 1)}
+    log(f"[bench] plain copy {2 * a.numel() / t_cp / 1e6:.0f} GB/s")
+    del a, bcp
+
+    # ---- CPU oracle on the host cores (a reported baseline, not the target) ----
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layer, enc)
+    print(json.dumps(out))
+
+
+def kernel_name(plan, m):
+    """Name of the GEMM kernel variant a plan launches, as rocprofv3 lists it."""
+    if plan["path"] == 1:
+        return f"w12::k_gemm<w12::GemvPath<{m}>>"
+    return f"w12::k_gemm<w12::MfmaPath<{plan['m_tile'] // 16}>>"
+
+
+def traffic_from_profile(alg):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, when it
+    matches the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M16_counters.txt")
+    if not os.path.exists(path):
+        return {"traffic": None}
+    with open(path) as f:
+        d = json.load(f)
+    src = os.path.join(ROOT, "lossless_bit_weight_encode_amd", "csrc", "w12_gemm.hip")
+    import hashlib
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if d.get("kernel_source_sha256") != digest:
+        return {"traffic": None, "traffic_note": "counters predate the current kernel source"}
+    return {"traffic": d["hbm_bytes_per_launch"], "traffic_over_alg": round(d["hbm_bytes_per_launch"] / alg, 4)}
+
+
+def summarize_trace(stats_csv, trace_csv, command):
+    """Kernel-time summary of a profiled --only-layer run: rocprofv3's per-kernel stats, plus the
+    GEMM durations split by matrix (the four layer GEMMs share one kernel name and are launched
+    in layer order)."""
+    import csv
+    with open(stats_csv) as f:
+        stats = list(csv.DictReader(f))
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    gemm = [r for r in trace if "k_gemm" in r["Kernel_Name"]]
+    lines = ["# W12 GEMM kernel times: one dense decoder layer (hidden 5120), M=16, MI355X", "",
+             "Command (run from the repository root):", "", "```", command, "```", "",
+             "## rocprofv3 --stats (all kernels of the run)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines += ["", "## GEMM launches by matrix (kernel trace, layer order qkv, o_proj, gate_up, down)", "",
+              "| matrix | kernel | launches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|---|"]
+    for i, nm in enumerate(S.LAYER_ORDER):
+        rows = gemm[i::len(S.LAYER_ORDER)]
+        d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
+        lines.append(f"| {nm} | `{rows[0]['Kernel_Name'].split('(')[0]}` | {len(d)} | {d.mean():.2f} | "
+                     f"{np.median(d):.2f} | {d.min():.2f} | {d.max():.2f} |")
+    path = os.path.join(ROOT, "profiles", "gemm_layer_M16_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the gate_up GEMM launches, each scaled by
+    the same counter's reading for the 256 MiB torch copy of the same run."""
+    import hashlib
+    copy_bytes = 256 << 20
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == name]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        # the layer step launches qkv, o_proj, gate_up, down in that order
+        gemms = [float(r["Counter_Value"]) for r in rows if "k_gemm" in r["Kernel_Name"]]
+        gate = gemms[S.LAYER_ORDER.index("gate_up")::len(S.LAYER_ORDER)]
+        probe = [float(r["Counter_Value"]) for r in rows if "elementwise" in r["Kernel_Name"].lower()]
+        if not gate or not probe:
+            raise SystemExit(f"{path}: no gate_up GEMM or elementwise probe dispatch found")
+        # the probe reads (FETCH) and writes (WRITE) exactly copy_bytes
+        scale = copy_bytes / (probe[-1] * 1024.0)
+        res[name] = {"gemm_kib_per_dispatch": gate, "copy_kib": probe[-1], "scale": scale}
+    layer_gemms = res["FETCH_SIZE"]["gemm_kib_per_dispatch"]
+    fetch = float(np.median(res["FETCH_SIZE"]["gemm_kib_per_dispatch"])) * 1024 * res["FETCH_SIZE"]["scale"]
+    write = float(np.median(res["WRITE_SIZE"]["gemm_kib_per_dispatch"])) * 1024 * res["WRITE_SIZE"]["scale"]
+    src = os.path.join(ROOT, "lossless_bit_weight_encode_amd", "csrc", "w12_gemm.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    out = {"kernel": "w12::k_gemm<w12::MfmaPath<1>> (M=16 launches of the layer step)",
+           "dispatches": len(layer_gemms), "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "hbm_bytes_per_launch": fetch + write,
+           "fetch_scale": res["FETCH_SIZE"]["scale"], "write_scale": res["WRITE_SIZE"]["scale"],
+           "kernel_source_sha256": digest,
+           "commands": [f"rocprofv3 --pmc {c} -f csv -d gpurun_out/pmc_{c.split('_')[0].lower()} -o run -- "
+                        "python3 bench.py --only-layer --steps 3 --warmup 1 --copy-probe"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                       [f"python3 bench.py --summarize-counters {fetch_csv} {write_csv}"],
+           "scaling": "each counter is scaled by 256 MiB / (its reading for the probe's elementwise kernel, "
+                      "which reads and writes exactly 256 MiB)"}
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M16_counters.txt")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def cpu_baseline(layer, enc):
+    """The oracle's decode + FP64 GEMM of gate_up at M=16 (the whole matrix), timed 3 times."""
+    from oracle import w12_oracle as O
+    w = layer["gate_up"]
+    n, k = w.shape
+    log("[bench] cpu baseline: oracle encode of gate_up")
+    ref = O.encode(w)
+    x = S.activations(16, k, S.x_seed(16, k))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        wd = O.decode(ref)
+        O.gemm_reference(x, wd)
+        times.append(time.perf_counter() - t0)
+        log(f"[bench] cpu baseline rep {times[-1]:.2f}s")
+    t = float(np.median(times))
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    return {
+        "value": round(2 * n * k / t / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": blas_threads, "kind": "oracle",
+        "sample": f"gate_up {n}x{k}, M=16: oracle decode + FP64 GEMM, median of 3 runs ({t:.2f} s each)",
+    }
+
+
+if __name__ == "__main__":
+    main()
