@@ -35,6 +35,7 @@ constexpr int kThreads = kWaves * kWave;
 constexpr int kSubRanges = kWaves * 4;
 constexpr int kUnitChunks = kSubRanges;   // chunks per stream-K unit (one per sub-range)
 constexpr int kRB = 4;                    // row blocks per tile (64 rows)
+constexpr int kTileRows = kRB * kRowsPerBlock;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any plane: reads give 0
 
 __device__ __forceinline__ int64_t split_point(int64_t total, int64_t parts, int64_t q) { return q * total / parts; }
@@ -56,7 +57,7 @@ struct GemmArgs {
   int64_t upt;          // units per tile
   int64_t units;        // tiles x upt
   int64_t G;            // work-groups
-  uint32_t hi_bytes, lo_bytes, x_bytes;
+  uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes;
   float* Y;
   int64_t ldy;
   uint32_t* counters;   // [tiles]
@@ -64,6 +65,9 @@ struct GemmArgs {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// The wave's index in the work-group, known to be uniform (scalar).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -85,6 +89,43 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint3
 // ------------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
+
+// Eight consecutive dwords at a (one statement, one wait).
+__device__ __forceinline__ void lds_read8(uint32_t a, uint32_t o[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %8 offset:0\nds_read_b32 %1, %8 offset:4\nds_read_b32 %2, %8 offset:8\n"
+      "ds_read_b32 %3, %8 offset:12\nds_read_b32 %4, %8 offset:16\nds_read_b32 %5, %8 offset:20\n"
+      "ds_read_b32 %6, %8 offset:24\nds_read_b32 %7, %8 offset:28\ns_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(a)
+      : "memory");
+}
+// MB 16-byte vectors 64 bytes apart at a (one statement, one wait).
+template <int MB>
+__device__ __forceinline__ void lds_read_mblocks(uint32_t a, uint4 o[MB]) {
+  if constexpr (MB == 1) {
+    asm volatile("ds_read_b128 %0, %1 offset:0\ns_waitcnt lgkmcnt(0)" : "=&v"(o[0]) : "v"(a) : "memory");
+  } else if constexpr (MB == 2) {
+    asm volatile("ds_read_b128 %0, %2 offset:0\nds_read_b128 %1, %2 offset:64\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]) : "v"(a) : "memory");
+  } else if constexpr (MB == 3) {
+    asm volatile("ds_read_b128 %0, %3 offset:0\nds_read_b128 %1, %3 offset:64\nds_read_b128 %2, %3 offset:128\n"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]) : "v"(a) : "memory");
+  } else {
+    asm volatile("ds_read_b128 %0, %4 offset:0\nds_read_b128 %1, %4 offset:64\nds_read_b128 %2, %4 offset:128\n"
+                 "ds_read_b128 %3, %4 offset:192\ns_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]) : "v"(a) : "memory");
+  }
+}
+__device__ __forceinline__ void lds_write_u32(uint32_t a, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_write_u128(uint32_t a, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};   // a native vector: asm inputs cannot be structs
+  asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(w) : "memory");
+}
 
 // Wait until at most N vector-memory instructions of this wave are outstanding.
 template <int N>
@@ -165,50 +206,6 @@ __device__ __forceinline__ void read_stage_wx(uint32_t ah, uint32_t al, uint32_t
 }
 
 // ------------------------------------------------------------------------------------------
-// Escapes: per lane and row block, a cursor over the channel's entries with k >= the start of
-// the lane's range.  Entries past the range are never reached (their k is beyond every chunk
-// the lane decodes), so the cursor needs no end of range.
-// ------------------------------------------------------------------------------------------
-struct LaneEsc {
-  uint32_t pos, end;   // next entry and end of the channel's list
-  uint32_t e;          // the entry at pos (valid when pos < end)
-};
-
-__device__ __forceinline__ void esc_start(LaneEsc& c, const GemmArgs& g, int64_t n, uint32_t k_lo) {
-  c.pos = c.end = 0;
-  c.e = 0;
-  if (n >= g.N) return;
-  uint32_t e_lo, e_hi;
-  escape_range(g.esc_ptr, n, g.num_esc, e_lo, e_hi);
-  const uint32_t cnt = e_hi - e_lo;
-  if (cnt == 0) return;
-  if (cnt <= 4) {
-    // the common case (about one escape per 5120 weights): four independent loads
-    uint32_t v[4], skip = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ((uint32_t)i < cnt) ? g.esc[e_lo + i] : 0xFFFFFFFFu;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) skip += ((uint32_t)i < cnt) && ((v[i] >> 16) < k_lo);
-    c.pos = e_lo + skip;
-    c.end = e_hi;
-    c.e = skip == 0 ? v[0] : (skip == 1 ? v[1] : (skip == 2 ? v[2] : v[3]));
-  } else {
-    c.pos = lower_bound_k(g.esc, e_lo, e_hi, k_lo);
-    c.end = e_hi;
-    c.e = c.pos < c.end ? g.esc[c.pos] : 0u;
-  }
-}
-
-// Patch every escape of this lane's row that falls in chunk [k0, k0 + 16).
-__device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict__ esc, uint32_t k0, uint32_t d[8]) {
-  while (c.pos < c.end && (c.e >> 16) < k0 + kChunkK) {
-    patch16(d, (c.e >> 16) - k0, c.e & 0xFFFFu);
-    ++c.pos;
-    c.e = c.pos < c.end ? esc[c.pos] : 0u;
-  }
-}
-
-// ------------------------------------------------------------------------------------------
 // LDS ring (per work-group; each wave owns its slice).  One object per stage lets the
 // compiler wait for exactly the stage being read.
 // ------------------------------------------------------------------------------------------
@@ -233,9 +230,11 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
   const int lane = threadIdx.x & 63, r = lane & 15;
   const uint32_t c = (sl.c_lo + j < sl.c_hi) ? sl.c_lo + j : sl.c_at;   // past the range: unused re-read
   const uint32_t vh = (c * kRowsPerBlock + r) * kChunkK;
+  // the row block's plane offset rides in the per-lane offset: a scalar soffset would need
+  // the compiler to prove it uniform, and it cannot once scalar registers run out
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)vh, (int)soff_h[rb], 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
   const uint32_t cd = (sl.cd_lo + j < sl.cd_hi) ? sl.cd_lo + j : sl.cd_at;
   const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
   dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
@@ -295,23 +294,33 @@ struct GemvPath {
     }
   }
   // Reduce over the 4 lane groups with a fixed butterfly, then add this wave's values into
-  // red[row][m] (waves in order 0..3, called once per wave in that order).
-  __device__ static void to_lds(Acc acc[], int rb, float* red, bool first_wave) {
+  // red[row][m] (waves in order 0..3, called once per wave in that order).  After the
+  // butterfly every lane group holds the sums of all 4 row blocks; lane group g writes row
+  // block g.
+  __device__ static void to_red(Acc acc[kRB][M], uint32_t red, bool first_wave) {
     const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
+    float v[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      float v = acc[m];
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      acc[m] = v;
-    }
-    if (gq == 0) {
+      float s4[kRB];
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float* dst = &red[(rb * kRowsPerBlock + r) * M + m];
-        *dst = first_wave ? acc[m] : *dst + acc[m];
+      for (int rb = 0; rb < kRB; ++rb) {
+        float x = acc[rb][m];
+        x += __shfl_xor(x, 16, kWave);
+        x += __shfl_xor(x, 32, kWave);
+        s4[rb] = x;
       }
+      v[m] = gq == 0 ? s4[0] : (gq == 1 ? s4[1] : (gq == 2 ? s4[2] : s4[3]));
     }
+    const uint32_t a = red + (uint32_t)(((gq * kRowsPerBlock + r) * M) * 4);
+    if (!first_wave) {
+      uint32_t o[8];
+      lds_read8(a, o);
+#pragma unroll
+      for (int m = 0; m < M; ++m) v[m] += __builtin_bit_cast(float, o[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) lds_write_u32(a + 4u * m, __builtin_bit_cast(uint32_t, v[m]));
   }
 };
 
@@ -349,77 +358,208 @@ struct MfmaPath {
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xb[mb]), b1, acc[mb], 0, 0, 0);
     }
   }
-  // lane (r, g) holds C[m = 4g + i][n = r] of each m block
-  __device__ static void to_lds(Acc acc[], int rb, float* red, bool first_wave) {
+  // lane (r, g) holds C[m = 4g + i][n = r] of each m block: 4 consecutive floats of red[row][m]
+  __device__ static void to_red(Acc acc[kRB][MB], uint32_t red, bool first_wave) {
     const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int rb = 0; rb < kRB; ++rb) {
+      const uint32_t a = red + (uint32_t)(((rb * kRowsPerBlock + r) * kMRows + 4 * gq) * 4);
+      uint4 o[MB];
+      if (!first_wave) lds_read_mblocks<MB>(a, o);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* dst = &red[(rb * kRowsPerBlock + r) * kMRows + mb * 16 + 4 * gq + i];
-        *dst = first_wave ? acc[mb][i] : *dst + acc[mb][i];
+      for (int mb = 0; mb < MB; ++mb) {
+        // named components: a bit_cast of a vector-element lvalue reads element 0
+        const f32x4 x = acc[rb][mb];
+        float v0 = x.x, v1 = x.y, v2 = x.z, v3 = x.w;
+        if (!first_wave) {
+          v0 += __builtin_bit_cast(float, o[mb].x);
+          v1 += __builtin_bit_cast(float, o[mb].y);
+          v2 += __builtin_bit_cast(float, o[mb].z);
+          v3 += __builtin_bit_cast(float, o[mb].w);
+        }
+        lds_write_u128(a + 64u * mb, make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                                                __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)));
       }
+    }
   }
 };
 
 // ------------------------------------------------------------------------------------------
-// Segment epilogue.  Cross-work-group visibility without cache-wide fences: the segments of
-// a tile may run on different XCDs, whose L2 caches are not coherent with each other.  Every
-// access to the partial buffer and to the arrival counter is a device-scope (agent) atomic
-// access, performed at the device coherence point (stores and loads carry sc1, the counter
-// RMW is device-coherent), and each wave waits for its partial stores to complete
-// (vmcnt(0)) before the barrier that precedes the counter increment.  Agent-scope
-// release/acquire fences would write back / invalidate the whole L2 of the XCD instead.
+// Cross-work-group visibility without cache-wide fences: the segments of a tile may run on
+// different XCDs, whose L2 caches are not coherent with each other.  Every access to the
+// partial buffer and to the arrival counters is a device-scope (agent) atomic access,
+// performed at the device coherence point (stores and loads carry sc1, the counter RMW is
+// device-coherent), and a work-group waits for its partial stores to complete (vmcnt(0))
+// before it bumps any counter.  Agent-scope release/acquire fences would write back /
+// invalidate the whole L2 of the XCD instead.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0xF70); /* vmcnt(0) */ }
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A barrier without the memory fence of __syncthreads (whose release part would wait for
+// every buffer-to-LDS load in flight); LDS writes are waited for explicitly before it.
+__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
+
+__device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
 
 // Stream-K bookkeeping: work-group w owns units [ubeg(w), ubeg(w+1)).
 __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w * g.units / g.G; }
 
-template <int ROWS, int MROWS>
-__device__ __forceinline__ void finish_segment(const GemmArgs& g, const float* red, int64_t tile, int64_t rg, int m0,
-                                               bool full, bool first_seg, uint32_t* s_flag) {
-  const int64_t n0 = rg * ROWS;
-  if (full) {
-    for (int i = threadIdx.x; i < ROWS * MROWS; i += kThreads) {
-      const int row = i / MROWS, ml = i % MROWS;
-      const int64_t n = n0 + row;
-      const int m = m0 + ml;
-      if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = red[i];
-    }
+// ------------------------------------------------------------------------------------------
+// Escapes.  Each segment's 64 channels have contiguous escape lists; the slice
+// [esc_ptr[row0], esc_ptr[row0 + 64]) is copied into LDS (up to kSliceEntries entries, one
+// 1 KB DMA per wave) while the previous segment streams, and every lane walks a cursor over
+// its channel's part of it.  A larger slice (dense escapes) is walked in global memory.
+// ------------------------------------------------------------------------------------------
+constexpr int kSliceEntries = kWaves * kWave * 4;   // 1024
+
+struct SegEsc {        // per lane, loaded one segment ahead
+  uint2 ptr[kRB];      // {esc_ptr[n], esc_ptr[n + 1]} of the lane's 4 channels
+  uint32_t base[kRB];  // window base of the lane's 4 channels
+};
+
+// The lane's channels of the segment on row group rg: esc_ptr pairs and bases, as buffer
+// loads (exactly 2 kRB vector-memory instructions); rows past N read as an empty list.
+__device__ __forceinline__ void load_seg_esc(const GemmArgs& g, __amdgpu_buffer_rsrc_t rp,
+                                             __amdgpu_buffer_rsrc_t rbase, int64_t rg, SegEsc& se) {
+  const int r = threadIdx.x & 15;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int64_t n = rg * kTileRows + rb * kRowsPerBlock + r;
+    const uint32_t po = n < g.N ? (uint32_t)n * 4u : kOutOfRange;
+    se.ptr[rb] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rp, (int)po, 0, 0));
+    se.base[rb] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rbase, (int)(n < g.N ? (uint32_t)n : kOutOfRange), 0, 0);
+  }
+}
+
+// Clamp a lane's list bounds into [0, E] (rows past N: empty at E).
+__device__ __forceinline__ void seg_bounds(const GemmArgs& g, int64_t rg, int rb, const SegEsc& se, uint32_t& lo,
+                                           uint32_t& hi) {
+  const int64_t n = rg * kTileRows + rb * kRowsPerBlock + (threadIdx.x & 15);
+  if (n >= g.N) {
+    lo = hi = g.num_esc;
     return;
   }
-  const int64_t w = blockIdx.x;
-  float* mine = g.P + (2 * w + (first_seg ? 0 : 1)) * (int64_t)(ROWS * MROWS);
-  for (int i = threadIdx.x; i < ROWS * MROWS; i += kThreads)
-    __hip_atomic_store(mine + i, red[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vm_all();
-  // segments of this tile: work-groups w_a..w_b
-  const int64_t t0 = tile * g.upt;
-  const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
-  const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
-  const uint32_t nseg = (uint32_t)(w_b - w_a + 1);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = (prev == nseg - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (*s_flag == 0) return;
-  for (int i = threadIdx.x; i < ROWS * MROWS; i += kThreads) {
-    const int row = i / MROWS, ml = i % MROWS;
-    const int64_t n = n0 + row;
-    const int m = m0 + ml;
-    float v = 0.f;
-    for (int64_t wj = w_a; wj <= w_b; ++wj) {
-      const int pos = ubeg(g, wj) >= t0 ? 0 : 1;   // the tile's segment is wj's first, else its last
-      const float p = __hip_atomic_load(g.P + (2 * wj + pos) * (int64_t)(ROWS * MROWS) + i, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-      v = (wj == w_a) ? p : v + p;
+  hi = se.ptr[rb].y < g.num_esc ? se.ptr[rb].y : g.num_esc;
+  lo = se.ptr[rb].x < hi ? se.ptr[rb].x : hi;
+}
+
+// First and end entry of the segment's slice (uniform): the lists of rows row0..row0+63.
+__device__ __forceinline__ void slice_range(const GemmArgs& g, int64_t rg, const SegEsc& se, uint32_t& s0,
+                                            uint32_t& s1) {
+  uint32_t lo0, hi0, lo3, hi3;
+  seg_bounds(g, rg, 0, se, lo0, hi0);
+  seg_bounds(g, rg, kRB - 1, se, lo3, hi3);
+  s0 = __builtin_amdgcn_readlane(lo0, 0);    // row0
+  s1 = __builtin_amdgcn_readlane(hi3, 15);   // row0 + 63 (or E past N)
+  s1 = s1 > s0 ? s1 : s0;
+}
+
+// One DMA per wave: entries [s0 + 256 wave, + 256) of the slice into LDS.
+__device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t re, uint32_t s0, uint4* slice, int wave) {
+  const int lane = threadIdx.x & 63;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)&slice[wave * kWave], 16,
+                                           (int)((s0 + (uint32_t)(wave * kWave * 4 + lane * 4)) * 4u), 0, 0, 0);
+}
+
+struct LaneEsc {
+  uint32_t pos, end;   // next entry and end of the channel's list (slice-relative in LDS mode)
+  uint32_t e;          // the entry at pos (valid when pos < end)
+};
+
+// Cursor at the first entry with k >= k_lo.
+__device__ __forceinline__ void esc_start(LaneEsc& c, const GemmArgs& g, uint32_t lo, uint32_t hi, uint32_t k_lo,
+                                          bool in_lds, uint32_t s0, uint32_t slice_addr) {
+  if (in_lds) {
+    uint32_t pos = lo - s0, end = hi - s0;
+    end = end < (uint32_t)kSliceEntries ? end : (uint32_t)kSliceEntries;   // only a malformed list exceeds it
+    uint32_t e = 0;
+    while (pos < end) {
+      e = lds_read_u32(slice_addr + 4u * pos);
+      if ((e >> 16) >= k_lo) break;
+      ++pos;
     }
-    if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+    c.pos = pos;
+    c.end = end;
+    c.e = e;
+  } else {
+    c.pos = lower_bound_k(g.esc, lo, hi, k_lo);
+    c.end = hi;
+    c.e = c.pos < c.end ? g.esc[c.pos] : 0u;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Patch every escape of this lane's row that falls in chunk [k0, k0 + 16).
+__device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict__ esc, uint32_t k0, uint32_t d[8],
+                                          bool in_lds, uint32_t slice_addr) {
+  while (c.pos < c.end && (c.e >> 16) < k0 + kChunkK) {
+    patch16(d, (c.e >> 16) - k0, c.e & 0xFFFFu);
+    ++c.pos;
+    if (c.pos < c.end) c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc[c.pos];
+  }
+}
+
+// Per-lane geometry of one segment (the stretch of one tile inside a work-group's range).
+struct SegGeo {
+  int64_t u, seg_end, tile, t0, rg;
+  int m0;
+  SegLane sl;
+  uint32_t soff_h[kRB];
+  uint32_t xc_lo, xc_hi;   // X chunk range of the lane group this lane fetches X for (GEMV)
+};
+
+__device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t u_end, SegGeo& s) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int q = wave * 4 + (lane >> 4);
+  s.u = u;
+  s.tile = u / g.upt;
+  s.t0 = s.tile * g.upt;
+  s.seg_end = u_end < s.t0 + g.upt ? u_end : s.t0 + g.upt;
+  s.rg = s.tile / g.MT;
+  s.m0 = (int)(s.tile - s.rg * g.MT);
+  // this segment's chunks [cs0, cs1) and this lane's sub-range of them
+  const int64_t cs0 = (u - s.t0) * kUnitChunks;
+  const int64_t cs1 = ((s.seg_end - s.t0) * kUnitChunks < g.Kc) ? (s.seg_end - s.t0) * kUnitChunks : g.Kc;
+  SegLane& sl = s.sl;
+  sl.c_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q));
+  sl.c_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q + 1));
+  sl.iters = (uint32_t)ceil_div(cs1 - cs0, kSubRanges);
+  const int qd = wave * 4 + ((lane >> 3) & 3);
+  sl.cd_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd));
+  sl.cd_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd + 1));
+  // past its range (or for an empty range) a lane re-reads an in-range chunk, unused
+  sl.c_at = sl.c_lo < (uint32_t)g.Kc ? sl.c_lo : (uint32_t)g.Kc - 1;
+  sl.cd_at = sl.cd_lo < (uint32_t)g.Kc ? sl.cd_lo : (uint32_t)g.Kc - 1;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    int64_t rbg = s.rg * kRB + rb;
+    rbg = rbg < g.Nb ? rbg : g.Nb - 1;   // a ragged last tile re-reads its last row block
+    s.soff_h[rb] = (uint32_t)(rbg * g.Kc * kHiChunkBytes);
+  }
+  {
+    int64_t rb0 = s.rg * kRB + (lane >> 5), rb1 = s.rg * kRB + 2 + (lane >> 5);
+    rb0 = rb0 < g.Nb ? rb0 : g.Nb - 1;
+    rb1 = rb1 < g.Nb ? rb1 : g.Nb - 1;
+    sl.lo_rb0 = (uint32_t)(rb0 * g.Kc * kLoChunkBytes);
+    sl.lo_rb1 = (uint32_t)(rb1 * g.Kc * kLoChunkBytes);
+  }
+  const int qx = wave * 4 + ((lane >> 1) & 3);
+  s.xc_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx));
+  s.xc_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx + 1));
+}
+
+// At most `pend` vector-memory instructions may remain outstanding (compile-time cases).
+template <int V>
+__device__ __forceinline__ void wait_pending(int pend) {
+  if (pend == V + 2 * kRB) wait_vmcnt<V + 2 * kRB>();
+  else if (pend == V + 1) wait_vmcnt<V + 1>();
+  else if (pend == V) wait_vmcnt<V>();
+  else if (pend == 2 * kRB) wait_vmcnt<2 * kRB>();
+  else if (pend == 1) wait_vmcnt<1>();
+  else wait_vmcnt<0>();
 }
 
 // ------------------------------------------------------------------------------------------
@@ -428,134 +568,218 @@ __device__ __forceinline__ void finish_segment(const GemmArgs& g, const float* r
 template <class Path>
 __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   constexpr int RB = kRB;
-  constexpr int ROWS = RB * kRowsPerBlock;
+  constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
+  constexpr int V = Path::kVmemPerStage;
+  constexpr int TILE_ELEMS = ROWS * MROWS;
   typedef typename Path::XStage XStage;
   __shared__ RingStage<RB> ring0, ring1;
   __shared__ XStage xring0, xring1;
+  __shared__ uint4 slices[2][kSliceEntries / 4];
+  __shared__ float red[TILE_ELEMS + 8];   // + 8: lds_read8 of the last row reads past its M values
   __shared__ uint32_t s_flag;
-  static_assert(sizeof(RingStage<RB>) >= ROWS * MROWS * sizeof(float), "reduction buffer aliases stage 0");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, gq = lane >> 4;
-  const int q = wave * 4 + gq;
+  const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(g.lo, g.lo_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.X, g.x_bytes);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(g.esc_ptr, (uint32_t)(g.N + 1) * 4u);
+  const __amdgpu_buffer_rsrc_t re = make_rsrc(g.esc, g.esc_bytes);
+  const __amdgpu_buffer_rsrc_t rbase = make_rsrc(g.base, (uint32_t)g.N);
 
-  int64_t u = ubeg(g, blockIdx.x);
-  const int64_t u_first = u;
+  const int64_t u_first = ubeg(g, blockIdx.x);
   const int64_t u_end = ubeg(g, (int64_t)blockIdx.x + 1);
-  while (u < u_end) {
-    const int64_t tile = u / g.upt;
-    const int64_t t0 = tile * g.upt;
-    const int64_t seg_end = u_end < t0 + g.upt ? u_end : t0 + g.upt;
-    const int64_t rg = tile / g.MT;
-    const int m0 = (int)(tile % g.MT) * MROWS;
-    // this segment's chunks [cs0, cs1) and this lane's sub-range of them
-    const int64_t cs0 = (u - t0) * kUnitChunks;
-    const int64_t cs1 = ((seg_end - t0) * kUnitChunks < g.Kc) ? (seg_end - t0) * kUnitChunks : g.Kc;
-    SegLane sl;
-    sl.c_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q));
-    sl.c_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q + 1));
-    sl.iters = (uint32_t)ceil_div(cs1 - cs0, kSubRanges);
-    const int qd = wave * 4 + ((lane >> 3) & 3);
-    sl.cd_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd));
-    sl.cd_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd + 1));
-    // past its range (or for an empty range) a lane re-reads an in-range chunk, unused
-    sl.c_at = sl.c_lo < (uint32_t)g.Kc ? sl.c_lo : (uint32_t)g.Kc - 1;
-    sl.cd_at = sl.cd_lo < (uint32_t)g.Kc ? sl.cd_lo : (uint32_t)g.Kc - 1;
-    const int64_t row0 = rg * ROWS;
-    uint32_t soff_h[RB], bb2[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      int64_t rbg = rg * RB + rb;
-      rbg = rbg < g.Nb ? rbg : g.Nb - 1;   // a ragged last tile re-reads its last row block
-      soff_h[rb] = (uint32_t)(rbg * g.Kc * kHiChunkBytes);
-      const int64_t n = row0 + rb * kRowsPerBlock + r;
-      bb2[rb] = base_pair(n < g.N ? g.base[n] : 1u);
-    }
-    {
-      int64_t rb0 = rg * RB + (lane >> 5), rb1 = rg * RB + 2 + (lane >> 5);
-      rb0 = rb0 < g.Nb ? rb0 : g.Nb - 1;
-      rb1 = rb1 < g.Nb ? rb1 : g.Nb - 1;
-      sl.lo_rb0 = (uint32_t)(rb0 * g.Kc * kLoChunkBytes);
-      sl.lo_rb1 = (uint32_t)(rb1 * g.Kc * kLoChunkBytes);
-    }
-    // X chunk range of the lane group this lane fetches X for (GEMV: lane / 2 % 4)
-    const int qx = wave * 4 + ((lane >> 1) & 3);
-    const uint32_t xc_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx));
-    const uint32_t xc_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx + 1));
+  if (u_first >= u_end) return;
 
-    // escape cursors first (their loads retire before the DMA issued after them)
-    LaneEsc cur[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) esc_start(cur[rb], g, row0 + rb * kRowsPerBlock + r, sl.c_lo * kChunkK);
+  uint32_t ah0, al0, ah1, al1;
+  ring_addr<RB>(&ring0, wave, ah0, al0);
+  ring_addr<RB>(&ring1, wave, ah1, al1);
+  const uint32_t slice_addr0 = lds_off(&slices[0][0]), slice_addr1 = lds_off(&slices[1][0]);
+  const uint32_t red_addr = lds_off(&red[0]);
 
-    // stage 0 (and X 0) in flight
-    issue_w<RB>(g, rh, rl, soff_h, sl, 0, &ring0, wave);
-    uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
-    if constexpr (Path::kXInLds) {
-      Path::issue_x(g, rx, xc_lo, xc_hi, 0, &xring0, wave);
-    } else {
-      Path::load_x(g, rx, m0, sl.c_lo, sl.c_lo < sl.c_hi, xa0, xb0);
-    }
+  // ---- prologue: the first segment's escape data, then its stage 0 ----
+  SegGeo cur;
+  seg_setup(g, u_first, u_end, cur);
+  SegEsc se;
+  load_seg_esc(g, rp, rbase, cur.rg, se);
+  uint32_t s0, s1;
+  slice_range(g, cur.rg, se, s0, s1);   // waits for the loads above
+  issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
+  uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
+  if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, 0, &xring0, wave);
+  else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo, cur.sl.c_lo < cur.sl.c_hi, xa0, xb0);
+  issue_slice(re, s0, &slices[0][0], wave);
+  wait_vmcnt<0>();
+  barrier();
+
+  int sb = 0;   // slice buffer of the current segment
+  bool in_lds = (s1 - s0) <= (uint32_t)kSliceEntries;
+  uint32_t bb2[RB];
+  LaneEsc cur_esc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    uint32_t lo, hi;
+    seg_bounds(g, cur.rg, rb, se, lo, hi);
+    bb2[rb] = base_pair(se.base[rb] ? se.base[rb] : 1u);
+    esc_start(cur_esc[rb], g, lo, hi, cur.sl.c_lo * kChunkK, in_lds, s0, slice_addr0);
+  }
+  int64_t pend0 = 0, pend1 = 0;   // tiles of the (at most two) partial segments
+  int npend = 0;
+
+  for (;;) {
+    const bool has_next = cur.seg_end < u_end;
+    const int64_t nrg = has_next ? (cur.tile + 1) / g.MT : 0;
+    SegEsc nse;
+    uint32_t ns0 = 0, ns1 = 0;
+    bool next_sliced = false;
     typename Path::Acc acc[RB][Path::kAcc];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) Path::zero(acc[rb]);
+    const uint32_t iters = cur.sl.iters;
 
-    uint32_t ah0, al0, ah1, al1;
-    ring_addr<RB>(&ring0, wave, ah0, al0);
-    ring_addr<RB>(&ring1, wave, ah1, al1);
-    // stage j is complete once at most `pending` newer vector-memory instructions remain
-    auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, bool pending) {
-      if (pending) wait_vmcnt<Path::kVmemPerStage>();
-      else wait_vmcnt<0>();
+    const uint32_t sl_addr = sb ? slice_addr1 : slice_addr0;
+    // stage j is complete once at most `pend` newer vector-memory instructions remain
+    auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
+      wait_pending<V>(pend);
       static_assert(RB == 4, "ring reads are written for 4 row blocks");
       uint4 h[RB];
       uint2 l[RB];
       if constexpr (Path::kXInLds) read_stage_wx<Path::kAcc>(ah, al, Path::x_addr(xs, wave), h, l, xa, xb);
       else read_stage_w(ah, al, h, l);
-      const uint32_t c = sl.c_lo + j;
-      const bool valid = c < sl.c_hi;
+      const uint32_t c = cur.sl.c_lo + j;
+      const bool valid = c < cur.sl.c_hi;
       const uint32_t k0 = c * kChunkK;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         uint32_t d[8];
         decode16(h[rb], l[rb], bb2[rb], d);
-        if (valid) esc_apply(cur[rb], g.esc, k0, d);
+        if (valid) esc_apply(cur_esc[rb], g.esc, k0, d, in_lds, sl_addr);
         Path::mac(d, xa, xb, acc[rb]);
       }
     };
-    for (uint32_t j = 0; j < sl.iters; j += 2) {
-      const bool more1 = j + 1 < sl.iters;
+    for (uint32_t j = 0; j < iters; j += 2) {
+      // even step: stage j in ring0
+      const bool more1 = j + 1 < iters;
+      int pend = 0;
       if (more1) {
-        issue_w<RB>(g, rh, rl, soff_h, sl, j + 1, &ring1, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, xc_lo, xc_hi, j + 1, &xring1, wave);
-        else Path::load_x(g, rx, m0, sl.c_lo + j + 1, sl.c_lo + j + 1 < sl.c_hi, xa1, xb1);
+        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, j + 1, &xring1, wave);
+        else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo + j + 1, cur.sl.c_lo + j + 1 < cur.sl.c_hi, xa1, xb1);
+        pend = V;
       }
-      compute(ah0, al0, &xring0, xa0, xb0, j, more1);
+      if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
+        load_seg_esc(g, rp, rbase, nrg, nse);
+        pend += 2 * RB;
+      }
+      compute(ah0, al0, &xring0, xa0, xb0, j, pend);
       if (!more1) break;
-      const bool more2 = j + 2 < sl.iters;
+      // odd step: stage j + 1 in ring1
+      const bool more2 = j + 2 < iters;
+      pend = 0;
       if (more2) {
-        issue_w<RB>(g, rh, rl, soff_h, sl, j + 2, &ring0, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, xc_lo, xc_hi, j + 2, &xring0, wave);
-        else Path::load_x(g, rx, m0, sl.c_lo + j + 2, sl.c_lo + j + 2 < sl.c_hi, xa0, xb0);
+        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, j + 2, &xring0, wave);
+        else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo + j + 2, cur.sl.c_lo + j + 2 < cur.sl.c_hi, xa0, xb0);
+        pend = V;
       }
-      compute(ah1, al1, &xring1, xa1, xb1, j + 1, more2);
+      if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
+        slice_range(g, nrg, nse, ns0, ns1);
+        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+        next_sliced = true;
+        pend += 1;
+      }
+      compute(ah1, al1, &xring1, xa1, xb1, j + 1, pend);
     }
-    __syncthreads();   // every wave is done with the ring; stage 0 becomes the reduction buffer
-    float* red = reinterpret_cast<float*>(&ring0);
+
+    // ---- segment end: the next segment's escape slice and stage 0, then the epilogue ----
+    SegGeo nxt;
+    if (has_next) {
+      if (!next_sliced) {
+        slice_range(g, nrg, nse, ns0, ns1);
+        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+      }
+      seg_setup(g, cur.seg_end, u_end, nxt);
+    }
+    wait_vmcnt<0>();   // this wave's slice part (and any stage) has landed
+    if (has_next) {
+      issue_w<RB>(g, rh, rl, nxt.soff_h, nxt.sl, 0, &ring0, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nxt.xc_lo, nxt.xc_hi, 0, &xring0, wave);
+      else Path::load_x(g, rx, nxt.m0 * MROWS, nxt.sl.c_lo, nxt.sl.c_lo < nxt.sl.c_hi, xa0, xb0);
+    }
+    // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
-      if (wave == w) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) Path::to_lds(acc[rb], rb, red, w == 0);
-      }
-      __syncthreads();
+      if (wave == w) Path::to_red(acc, red_addr, w == 0);
+      wait_lgkm();
+      barrier();
     }
-    const bool full = (u == t0) && (seg_end == t0 + g.upt);
-    finish_segment<ROWS, MROWS>(g, red, tile, rg, m0, full, u == u_first, &s_flag);
-    __syncthreads();   // LDS is reused by the next segment
-    u = seg_end;
+    const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
+    const int m0 = cur.m0 * MROWS;
+    const int pos = (cur.u == u_first) ? 0 : 1;   // partial slot: the work-group's first or last segment
+    float* mine = g.P + (2 * (int64_t)blockIdx.x + pos) * (int64_t)TILE_ELEMS;
+    for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
+      const int row = e % ROWS, ml = e / ROWS;
+      const float v = __builtin_bit_cast(float, lds_read_u32(red_addr + (uint32_t)((row * MROWS + ml) * 4)));
+      if (full) {
+        const int64_t n = cur.rg * ROWS + row;
+        const int m = m0 + ml;
+        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+      } else {
+        __hip_atomic_store(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (!full) {
+      if (npend == 0) pend0 = cur.tile; else pend1 = cur.tile;
+      ++npend;
+    }
+    if (!has_next) break;
+    barrier();   // red is free again; the next slice is visible to every wave
+    // switch to the next segment
+    cur = nxt;
+    sb ^= 1;
+    in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t lo, hi;
+      seg_bounds(g, cur.rg, rb, nse, lo, hi);
+      bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
+      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c_lo * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+    }
+  }
+
+  // ---- deferred split-K: bump the counters of partial tiles; the last arriver sums ----
+  wait_vm_all();
+  __syncthreads();
+  for (int p = 0; p < npend; ++p) {
+    const int64_t tile = p == 0 ? pend0 : pend1;
+    const int64_t t0 = tile * g.upt;
+    const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
+    const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
+    const uint32_t nsegs = (uint32_t)(w_b - w_a + 1);
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag = (prev == nsegs - 1) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_flag) {
+      const int64_t rg = tile / g.MT;
+      const int m0 = (int)(tile - rg * g.MT) * MROWS;
+      // the tile is the first segment of every contributor except possibly w_a
+      const int pos_a = ubeg(g, w_a) < t0 ? 1 : 0;
+      for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
+        float v = 0.f;
+        for (int64_t wj = w_a; wj <= w_b; ++wj) {
+          const int pos = wj == w_a ? pos_a : 0;
+          const float pv = __hip_atomic_load(g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS + e, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+          v = (wj == w_a) ? pv : v + pv;
+        }
+        const int row = e % ROWS, ml = e / ROWS;
+        const int64_t n = rg * ROWS + row;
+        const int m = m0 + ml;
+        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
   }
 }
 
@@ -751,6 +975,7 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   a.hi_bytes = (uint32_t)(chunks * kHiChunkBytes);
   a.lo_bytes = (uint32_t)(chunks * kLoChunkBytes);
   a.x_bytes = (uint32_t)(((uint64_t)(M - 1) * (uint64_t)ldx + (uint64_t)a.Kc * kChunkK) * 2u);
+  a.esc_bytes = (uint32_t)((uint64_t)t->num_escapes * 4u);
   a.Y = Y;
   a.ldy = ldy;
   a.counters = reinterpret_cast<uint32_t*>(ws);
