@@ -399,6 +399,11 @@ __device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)
 // every buffer-to-LDS load in flight); LDS writes are waited for explicitly before it.
 __device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
 
+__device__ __forceinline__ uint4 lds_read_u128(uint32_t a) {
+  uint4 v;
+  asm volatile("ds_read_b128 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
 __device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
   uint32_t v;
   asm volatile("ds_read_b32 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
@@ -715,15 +720,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     const int m0 = cur.m0 * MROWS;
     const int pos = (cur.u == u_first) ? 0 : 1;   // partial slot: the work-group's first or last segment
     float* mine = g.P + (2 * (int64_t)blockIdx.x + pos) * (int64_t)TILE_ELEMS;
-    for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
-      const int row = e % ROWS, ml = e / ROWS;
-      const float v = __builtin_bit_cast(float, lds_read_u32(red_addr + (uint32_t)((row * MROWS + ml) * 4)));
+    // partial tiles are stored in red's own layout [row][m], 4 consecutive elements per thread
+    for (int e = 4 * (int)threadIdx.x; e < TILE_ELEMS; e += 4 * kThreads) {
+      const uint4 q4 = lds_read_u128(red_addr + (uint32_t)(e * 4));
+      const float v[4] = {__builtin_bit_cast(float, q4.x), __builtin_bit_cast(float, q4.y),
+                          __builtin_bit_cast(float, q4.z), __builtin_bit_cast(float, q4.w)};
       if (full) {
-        const int64_t n = cur.rg * ROWS + row;
-        const int m = m0 + ml;
-        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = (e + q) / MROWS, ml = (e + q) % MROWS;
+          const int64_t n = cur.rg * ROWS + row;
+          const int m = m0 + ml;
+          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[q];
+        }
       } else {
-        __hip_atomic_store(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) __hip_atomic_store(mine + e + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (!full) {
@@ -764,18 +776,40 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       const int m0 = (int)(tile - rg * g.MT) * MROWS;
       // the tile is the first segment of every contributor except possibly w_a
       const int pos_a = ubeg(g, w_a) < t0 ? 1 : 0;
-      for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
-        float v = 0.f;
-        for (int64_t wj = w_a; wj <= w_b; ++wj) {
-          const int pos = wj == w_a ? pos_a : 0;
-          const float pv = __hip_atomic_load(g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS + e, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-          v = (wj == w_a) ? pv : v + pv;
+      // every load of a batch is issued before any is summed (one memory round trip per
+      // batch); the sum still runs in work-group order
+      constexpr int kBatch = 16;
+      const int64_t ns = w_b - w_a + 1;
+      for (int e = 4 * (int)threadIdx.x; e < TILE_ELEMS; e += 4 * kThreads) {
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t b0 = 0; b0 < ns; b0 += kBatch) {
+          float pv[kBatch][4];
+#pragma unroll
+          for (int sg = 0; sg < kBatch; ++sg) {
+            if (b0 + sg < ns) {
+              const int64_t wj = w_a + b0 + sg;
+              const int pos = wj == w_a ? pos_a : 0;
+              const float* src = g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS + e;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                pv[sg][q] = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+#pragma unroll
+          for (int sg = 0; sg < kBatch; ++sg) {
+            if (b0 + sg < ns) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = (b0 + sg == 0) ? pv[sg][q] : v[q] + pv[sg][q];
+            }
+          }
         }
-        const int row = e % ROWS, ml = e / ROWS;
-        const int64_t n = rg * ROWS + row;
-        const int m = m0 + ml;
-        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = (e + q) / MROWS, ml = (e + q) % MROWS;
+          const int64_t n = rg * ROWS + row;
+          const int m = m0 + ml;
+          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[q];
+        }
       }
       if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
