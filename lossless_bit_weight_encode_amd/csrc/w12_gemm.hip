@@ -90,32 +90,41 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint3
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
 
-// Eight consecutive dwords at a (one statement, one wait).
-__device__ __forceinline__ void lds_read8(uint32_t a, uint32_t o[8]) {
-  asm volatile(
-      "ds_read_b32 %0, %8 offset:0\nds_read_b32 %1, %8 offset:4\nds_read_b32 %2, %8 offset:8\n"
-      "ds_read_b32 %3, %8 offset:12\nds_read_b32 %4, %8 offset:16\nds_read_b32 %5, %8 offset:20\n"
-      "ds_read_b32 %6, %8 offset:24\nds_read_b32 %7, %8 offset:28\ns_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(a)
-      : "memory");
+// Batched LDS reads with literal offsets, one statement and one wait each (no register still
+// in flight is ever visible to the compiler).
+// M dwords 256 bytes apart (GEMV partials: one channel, M rows of X, red laid out [m][64]).
+template <int M>
+__device__ __forceinline__ void lds_read_m(uint32_t a, uint32_t o[M]) {
+  if constexpr (M == 1) {
+    asm volatile("ds_read_b32 %0, %1 offset:0\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]) : "v"(a) : "memory");
+  } else if constexpr (M == 2) {
+    asm volatile("ds_read_b32 %0, %2 offset:0\n""ds_read_b32 %1, %2 offset:256\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]) : "v"(a) : "memory");
+  } else if constexpr (M == 3) {
+    asm volatile("ds_read_b32 %0, %3 offset:0\n""ds_read_b32 %1, %3 offset:256\n""ds_read_b32 %2, %3 offset:512\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]) : "v"(a) : "memory");
+  } else if constexpr (M == 4) {
+    asm volatile("ds_read_b32 %0, %4 offset:0\n""ds_read_b32 %1, %4 offset:256\n""ds_read_b32 %2, %4 offset:512\n""ds_read_b32 %3, %4 offset:768\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]) : "v"(a) : "memory");
+  } else if constexpr (M == 5) {
+    asm volatile("ds_read_b32 %0, %5 offset:0\n""ds_read_b32 %1, %5 offset:256\n""ds_read_b32 %2, %5 offset:512\n""ds_read_b32 %3, %5 offset:768\n""ds_read_b32 %4, %5 offset:1024\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]) : "v"(a) : "memory");
+  } else if constexpr (M == 6) {
+    asm volatile("ds_read_b32 %0, %6 offset:0\n""ds_read_b32 %1, %6 offset:256\n""ds_read_b32 %2, %6 offset:512\n""ds_read_b32 %3, %6 offset:768\n""ds_read_b32 %4, %6 offset:1024\n""ds_read_b32 %5, %6 offset:1280\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]) : "v"(a) : "memory");
+  } else if constexpr (M == 7) {
+    asm volatile("ds_read_b32 %0, %7 offset:0\n""ds_read_b32 %1, %7 offset:256\n""ds_read_b32 %2, %7 offset:512\n""ds_read_b32 %3, %7 offset:768\n""ds_read_b32 %4, %7 offset:1024\n""ds_read_b32 %5, %7 offset:1280\n""ds_read_b32 %6, %7 offset:1536\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]) : "v"(a) : "memory");
+  } else if constexpr (M == 8) {
+    asm volatile("ds_read_b32 %0, %8 offset:0\n""ds_read_b32 %1, %8 offset:256\n""ds_read_b32 %2, %8 offset:512\n""ds_read_b32 %3, %8 offset:768\n""ds_read_b32 %4, %8 offset:1024\n""ds_read_b32 %5, %8 offset:1280\n""ds_read_b32 %6, %8 offset:1536\n""ds_read_b32 %7, %8 offset:1792\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]) : "v"(a) : "memory");
+  }
 }
-// MB 16-byte vectors 64 bytes apart at a (one statement, one wait).
+// 4 MB dwords of one row block (MFMA partials: rows 16 mb + 4 g + i, i < 4, 256 bytes apart
+// per row of X, 4 KB per m block).
 template <int MB>
-__device__ __forceinline__ void lds_read_mblocks(uint32_t a, uint4 o[MB]) {
+__device__ __forceinline__ void lds_read_mb(uint32_t a, uint32_t o[4 * MB]) {
   if constexpr (MB == 1) {
-    asm volatile("ds_read_b128 %0, %1 offset:0\ns_waitcnt lgkmcnt(0)" : "=&v"(o[0]) : "v"(a) : "memory");
+    asm volatile("ds_read_b32 %0, %4 offset:0\n""ds_read_b32 %1, %4 offset:256\n""ds_read_b32 %2, %4 offset:512\n""ds_read_b32 %3, %4 offset:768\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]) : "v"(a) : "memory");
   } else if constexpr (MB == 2) {
-    asm volatile("ds_read_b128 %0, %2 offset:0\nds_read_b128 %1, %2 offset:64\ns_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]) : "v"(a) : "memory");
+    asm volatile("ds_read_b32 %0, %8 offset:0\n""ds_read_b32 %1, %8 offset:256\n""ds_read_b32 %2, %8 offset:512\n""ds_read_b32 %3, %8 offset:768\n""ds_read_b32 %4, %8 offset:4096\n""ds_read_b32 %5, %8 offset:4352\n""ds_read_b32 %6, %8 offset:4608\n""ds_read_b32 %7, %8 offset:4864\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]) : "v"(a) : "memory");
   } else if constexpr (MB == 3) {
-    asm volatile("ds_read_b128 %0, %3 offset:0\nds_read_b128 %1, %3 offset:64\nds_read_b128 %2, %3 offset:128\n"
-                 "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]) : "v"(a) : "memory");
-  } else {
-    asm volatile("ds_read_b128 %0, %4 offset:0\nds_read_b128 %1, %4 offset:64\nds_read_b128 %2, %4 offset:128\n"
-                 "ds_read_b128 %3, %4 offset:192\ns_waitcnt lgkmcnt(0)"
-                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]) : "v"(a) : "memory");
+    asm volatile("ds_read_b32 %0, %12 offset:0\n""ds_read_b32 %1, %12 offset:256\n""ds_read_b32 %2, %12 offset:512\n""ds_read_b32 %3, %12 offset:768\n""ds_read_b32 %4, %12 offset:4096\n""ds_read_b32 %5, %12 offset:4352\n""ds_read_b32 %6, %12 offset:4608\n""ds_read_b32 %7, %12 offset:4864\n""ds_read_b32 %8, %12 offset:8192\n""ds_read_b32 %9, %12 offset:8448\n""ds_read_b32 %10, %12 offset:8704\n""ds_read_b32 %11, %12 offset:8960\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]) : "v"(a) : "memory");
+  } else if constexpr (MB == 4) {
+    asm volatile("ds_read_b32 %0, %16 offset:0\n""ds_read_b32 %1, %16 offset:256\n""ds_read_b32 %2, %16 offset:512\n""ds_read_b32 %3, %16 offset:768\n""ds_read_b32 %4, %16 offset:4096\n""ds_read_b32 %5, %16 offset:4352\n""ds_read_b32 %6, %16 offset:4608\n""ds_read_b32 %7, %16 offset:4864\n""ds_read_b32 %8, %16 offset:8192\n""ds_read_b32 %9, %16 offset:8448\n""ds_read_b32 %10, %16 offset:8704\n""ds_read_b32 %11, %16 offset:8960\n""ds_read_b32 %12, %16 offset:12288\n""ds_read_b32 %13, %16 offset:12544\n""ds_read_b32 %14, %16 offset:12800\n""ds_read_b32 %15, %16 offset:13056\n" "s_waitcnt lgkmcnt(0)" : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15]) : "v"(a) : "memory");
   }
 }
 __device__ __forceinline__ void lds_write_u32(uint32_t a, uint32_t v) {
@@ -294,7 +303,7 @@ struct GemvPath {
     }
   }
   // Reduce over the 4 lane groups with a fixed butterfly, then add this wave's values into
-  // red[row][m] (waves in order 0..3, called once per wave in that order).  After the
+  // red[m][row] (waves in order 0..3, called once per wave in that order).  After the
   // butterfly every lane group holds the sums of all 4 row blocks; lane group g writes row
   // block g.
   __device__ static void to_red(Acc acc[kRB][M], uint32_t red, bool first_wave) {
@@ -312,15 +321,15 @@ struct GemvPath {
       }
       v[m] = gq == 0 ? s4[0] : (gq == 1 ? s4[1] : (gq == 2 ? s4[2] : s4[3]));
     }
-    const uint32_t a = red + (uint32_t)(((gq * kRowsPerBlock + r) * M) * 4);
+    const uint32_t a = red + (uint32_t)((gq * kRowsPerBlock + r) * 4);
     if (!first_wave) {
-      uint32_t o[8];
-      lds_read8(a, o);
+      uint32_t o[M];
+      lds_read_m<M>(a, o);
 #pragma unroll
       for (int m = 0; m < M; ++m) v[m] += __builtin_bit_cast(float, o[m]);
     }
 #pragma unroll
-    for (int m = 0; m < M; ++m) lds_write_u32(a + 4u * m, __builtin_bit_cast(uint32_t, v[m]));
+    for (int m = 0; m < M; ++m) lds_write_u32(a + 256u * m, __builtin_bit_cast(uint32_t, v[m]));
   }
 };
 
@@ -358,27 +367,24 @@ struct MfmaPath {
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xb[mb]), b1, acc[mb], 0, 0, 0);
     }
   }
-  // lane (r, g) holds C[m = 4g + i][n = r] of each m block: 4 consecutive floats of red[row][m]
+  // lane (r, g) holds C[m = 16 mb + 4 g + i][n = 16 rb + r]: red[m][row] at m * 64 + row
   __device__ static void to_red(Acc acc[kRB][MB], uint32_t red, bool first_wave) {
     const int lane = threadIdx.x & 63, r = lane & 15, gq = lane >> 4;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      const uint32_t a = red + (uint32_t)(((rb * kRowsPerBlock + r) * kMRows + 4 * gq) * 4);
-      uint4 o[MB];
-      if (!first_wave) lds_read_mblocks<MB>(a, o);
+      const uint32_t a = red + (uint32_t)((4 * gq * kTileRows + rb * kRowsPerBlock + r) * 4);
+      uint32_t o[4 * MB];
+      if (!first_wave) lds_read_mb<MB>(a, o);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         // named components: a bit_cast of a vector-element lvalue reads element 0
         const f32x4 x = acc[rb][mb];
-        float v0 = x.x, v1 = x.y, v2 = x.z, v3 = x.w;
-        if (!first_wave) {
-          v0 += __builtin_bit_cast(float, o[mb].x);
-          v1 += __builtin_bit_cast(float, o[mb].y);
-          v2 += __builtin_bit_cast(float, o[mb].z);
-          v3 += __builtin_bit_cast(float, o[mb].w);
+        float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (!first_wave) v[i] += __builtin_bit_cast(float, o[4 * mb + i]);
+          lds_write_u32(a + (uint32_t)(mb * 4096 + i * 256), __builtin_bit_cast(uint32_t, v[i]));
         }
-        lds_write_u128(a + 64u * mb, make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
-                                                __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)));
       }
     }
   }
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   __shared__ RingStage<RB> ring0, ring1;
   __shared__ XStage xring0, xring1;
   __shared__ uint4 slices[2][kSliceEntries / 4];
-  __shared__ float red[TILE_ELEMS + 8];   // + 8: lds_read8 of the last row reads past its M values
+  __shared__ float red[TILE_ELEMS];
   __shared__ uint32_t s_flag;
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
@@ -720,22 +726,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     const int m0 = cur.m0 * MROWS;
     const int pos = (cur.u == u_first) ? 0 : 1;   // partial slot: the work-group's first or last segment
     float* mine = g.P + (2 * (int64_t)blockIdx.x + pos) * (int64_t)TILE_ELEMS;
-    // partial tiles are stored in red's own layout [row][m], 4 consecutive elements per thread
-    for (int e = 4 * (int)threadIdx.x; e < TILE_ELEMS; e += 4 * kThreads) {
-      const uint4 q4 = lds_read_u128(red_addr + (uint32_t)(e * 4));
-      const float v[4] = {__builtin_bit_cast(float, q4.x), __builtin_bit_cast(float, q4.y),
-                          __builtin_bit_cast(float, q4.z), __builtin_bit_cast(float, q4.w)};
+    // red, the partial tiles and Y's rows share the order e = m * 64 + row: consecutive threads
+    // touch consecutive channels
+    for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
+      const float v = __builtin_bit_cast(float, lds_read_u32(red_addr + (uint32_t)(e * 4)));
       if (full) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = (e + q) / MROWS, ml = (e + q) % MROWS;
-          const int64_t n = cur.rg * ROWS + row;
-          const int m = m0 + ml;
-          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[q];
-        }
+        const int row = e % ROWS, ml = e / ROWS;
+        const int64_t n = cur.rg * ROWS + row;
+        const int m = m0 + ml;
+        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
       } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) __hip_atomic_store(mine + e + q, v[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (!full) {
@@ -776,39 +777,45 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       const int m0 = (int)(tile - rg * g.MT) * MROWS;
       // the tile is the first segment of every contributor except possibly w_a
       const int pos_a = ubeg(g, w_a) < t0 ? 1 : 0;
-      // every load of a batch is issued before any is summed (one memory round trip per
-      // batch); the sum still runs in work-group order
-      constexpr int kBatch = 16;
+      // every load of a batch (up to 64 per thread: KB <= 16 contributors x ET elements) is issued
+      // before any is summed; the sum still runs in work-group order
+      constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;
+      constexpr int KB = ET >= 64 ? 1 : (64 / ET < 16 ? 64 / ET : 16);
       const int64_t ns = w_b - w_a + 1;
-      for (int e = 4 * (int)threadIdx.x; e < TILE_ELEMS; e += 4 * kThreads) {
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t b0 = 0; b0 < ns; b0 += kBatch) {
-          float pv[kBatch][4];
+      float v[ET];
 #pragma unroll
-          for (int sg = 0; sg < kBatch; ++sg) {
-            if (b0 + sg < ns) {
-              const int64_t wj = w_a + b0 + sg;
-              const int pos = wj == w_a ? pos_a : 0;
-              const float* src = g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS + e;
+      for (int k = 0; k < ET; ++k) v[k] = 0.f;
+      for (int64_t b0 = 0; b0 < ns; b0 += KB) {
+        float pv[KB][ET];
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                pv[sg][q] = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
+        for (int sg = 0; sg < KB; ++sg) {
+          if (b0 + sg < ns) {
+            const int64_t wj = w_a + b0 + sg;
+            const int pos = wj == w_a ? pos_a : 0;
+            const float* src = g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS;
 #pragma unroll
-          for (int sg = 0; sg < kBatch; ++sg) {
-            if (b0 + sg < ns) {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = (b0 + sg == 0) ? pv[sg][q] : v[q] + pv[sg][q];
+            for (int k = 0; k < ET; ++k) {
+              const int e = (int)threadIdx.x + k * kThreads;
+              if (e < TILE_ELEMS) pv[sg][k] = __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
           }
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = (e + q) / MROWS, ml = (e + q) % MROWS;
+        for (int sg = 0; sg < KB; ++sg) {
+          if (b0 + sg < ns) {
+#pragma unroll
+            for (int k = 0; k < ET; ++k) v[k] = (b0 + sg == 0) ? pv[sg][k] : v[k] + pv[sg][k];
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < ET; ++k) {
+        const int e = (int)threadIdx.x + k * kThreads;
+        if (e < TILE_ELEMS) {
+          const int row = e % ROWS, ml = e / ROWS;
           const int64_t n = rg * ROWS + row;
           const int m = m0 + ml;
-          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[q];
+          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[k];
         }
       }
       if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
