@@ -225,11 +225,19 @@ struct RingStage {
 };
 
 // Per-lane addressing of one segment.
+// Step j of a segment gives lane group q (= 4 wave + lane / 16) chunk c0 + stride * j, valid
+// while below c_end.  Two mappings of the segment's chunks [cs0, cs1) onto the 16 lane groups:
+//  * interleaved (stride 16, c0 = cs0 + q): a wave's 4 lane groups read 4 consecutive chunks,
+//    so its W bytes of a row block and X bytes of a row are contiguous;
+//  * contiguous (stride 1, c0 = the start of q's share): each lane group walks its own stretch
+//    of k, so its escape cursor only meets its own entries - used when the segment's escape
+//    lists do not fit in LDS and are walked in global memory.
+// A lane past c_end keeps reading the following chunks (inside the plane, or past it and then
+// zero); that data is unused: its X is zero and its escapes are skipped.
 struct SegLane {
-  uint32_t c_lo, c_hi, iters;   // this lane's chunks [c_lo, c_hi) (may be empty); iterations
-  uint32_t c_at;                // an in-range chunk to read when past the range
-  uint32_t cd_lo, cd_hi, cd_at; // the same for lane group (lane >> 3) & 3 (lo DMA)
-  uint32_t lo_rb0, lo_rb1;      // lo plane offsets of the row blocks this lane DMAs
+  uint32_t c0, c_end, stride, iters;   // this lane group's chunks
+  uint32_t cd0;                        // the same for lane group 4 wave + (lane >> 3) % 4 (lo DMA)
+  uint32_t lo_rb0, lo_rb1;             // lo plane offsets of the row blocks this lane copies
 };
 
 template <int RB>
@@ -237,14 +245,14 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
                                         const uint32_t soff_h[RB], const SegLane& sl, uint32_t j,
                                         RingStage<RB>* st, int wave) {
   const int lane = threadIdx.x & 63, r = lane & 15;
-  const uint32_t c = (sl.c_lo + j < sl.c_hi) ? sl.c_lo + j : sl.c_at;   // past the range: unused re-read
+  const uint32_t c = sl.c0 + sl.stride * j;
   const uint32_t vh = (c * kRowsPerBlock + r) * kChunkK;
   // the row block's plane offset rides in the per-lane offset: a scalar soffset would need
   // the compiler to prove it uniform, and it cannot once scalar registers run out
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
-  const uint32_t cd = (sl.cd_lo + j < sl.cd_hi) ? sl.cd_lo + j : sl.cd_at;
+  const uint32_t cd = sl.cd0 + sl.stride * j;
   const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
   dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
   if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
@@ -274,12 +282,12 @@ struct GemvPath {
     uint4 x[kWaves][kWave];   // [m][g][half]
   };
   // lanes l < 8M fetch (m = l / 8, lane group l / 2 % 4, half l % 2)
-  __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, const uint32_t xc_lo,
-                                 const uint32_t xc_hi, uint32_t j, XStage* xs, int wave) {
+  __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, uint32_t xc0, uint32_t xc_end,
+                                 uint32_t stride, uint32_t j, XStage* xs, int wave) {
     const int lane = threadIdx.x & 63;
     const uint32_t m = (uint32_t)lane >> 3, half = lane & 1;
-    const uint32_t c = xc_lo + j;
-    const uint32_t off = (m < (uint32_t)M && c < xc_hi) ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
+    const uint32_t c = xc0 + stride * j;
+    const uint32_t off = (m < (uint32_t)M && c < xc_end) ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
                                                         : kOutOfRange;
     dma16(rx, &xs->x[wave][0], off);
   }
@@ -503,11 +511,12 @@ __device__ __forceinline__ void esc_start(LaneEsc& c, const GemmArgs& g, uint32_
   }
 }
 
-// Patch every escape of this lane's row that falls in chunk [k0, k0 + 16).
+// Patch every escape of this lane's row that falls in chunk [k0, k0 + 16); entries below k0
+// belong to other lane groups' chunks (interleaved mapping) and are stepped over.
 __device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict__ esc, uint32_t k0, uint32_t d[8],
                                           bool in_lds, uint32_t slice_addr) {
   while (c.pos < c.end && (c.e >> 16) < k0 + kChunkK) {
-    patch16(d, (c.e >> 16) - k0, c.e & 0xFFFFu);
+    if ((c.e >> 16) >= k0) patch16(d, (c.e >> 16) - k0, c.e & 0xFFFFu);
     ++c.pos;
     if (c.pos < c.end) c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc[c.pos];
   }
@@ -519,10 +528,10 @@ struct SegGeo {
   int m0;
   SegLane sl;
   uint32_t soff_h[kRB];
-  uint32_t xc_lo, xc_hi;   // X chunk range of the lane group this lane fetches X for (GEMV)
+  uint32_t xc0, xc_end;    // chunks of the lane group this lane fetches X for (GEMV: 4 wave + lane / 2 % 4)
 };
 
-__device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t u_end, SegGeo& s) {
+__device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t u_end, bool interleaved, SegGeo& s) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int q = wave * 4 + (lane >> 4);
   s.u = u;
@@ -531,19 +540,29 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t 
   s.seg_end = u_end < s.t0 + g.upt ? u_end : s.t0 + g.upt;
   s.rg = s.tile / g.MT;
   s.m0 = (int)(s.tile - s.rg * g.MT);
-  // this segment's chunks [cs0, cs1) and this lane's sub-range of them
+  // this segment's chunks [cs0, cs1) and this lane group's share of them
   const int64_t cs0 = (u - s.t0) * kUnitChunks;
   const int64_t cs1 = ((s.seg_end - s.t0) * kUnitChunks < g.Kc) ? (s.seg_end - s.t0) * kUnitChunks : g.Kc;
   SegLane& sl = s.sl;
-  sl.c_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q));
-  sl.c_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q + 1));
-  sl.iters = (uint32_t)ceil_div(cs1 - cs0, kSubRanges);
   const int qd = wave * 4 + ((lane >> 3) & 3);
-  sl.cd_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd));
-  sl.cd_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd + 1));
-  // past its range (or for an empty range) a lane re-reads an in-range chunk, unused
-  sl.c_at = sl.c_lo < (uint32_t)g.Kc ? sl.c_lo : (uint32_t)g.Kc - 1;
-  sl.cd_at = sl.cd_lo < (uint32_t)g.Kc ? sl.cd_lo : (uint32_t)g.Kc - 1;
+  const int qx = wave * 4 + ((lane >> 1) & 3);
+  sl.c_end = (uint32_t)cs1;
+  sl.iters = (uint32_t)ceil_div(cs1 - cs0, kSubRanges);
+  if (interleaved) {
+    sl.stride = kSubRanges;
+    sl.c0 = (uint32_t)(cs0 + q);
+    sl.cd0 = (uint32_t)(cs0 + qd);
+    s.xc0 = (uint32_t)(cs0 + qx);
+    s.xc_end = (uint32_t)cs1;
+  } else {
+    sl.stride = 1;
+    sl.c0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q));
+    sl.cd0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd));
+    s.xc0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx));
+    s.xc_end = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx + 1));
+    // a contiguous share ends where the next lane group's begins
+    sl.c_end = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q + 1));
+  }
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     int64_t rbg = s.rg * kRB + rb;
@@ -557,9 +576,6 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t 
     sl.lo_rb0 = (uint32_t)(rb0 * g.Kc * kLoChunkBytes);
     sl.lo_rb1 = (uint32_t)(rb1 * g.Kc * kLoChunkBytes);
   }
-  const int qx = wave * 4 + ((lane >> 1) & 3);
-  s.xc_lo = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx));
-  s.xc_hi = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx + 1));
 }
 
 // At most `pend` vector-memory instructions may remain outstanding (compile-time cases).
@@ -609,15 +625,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
 
   // ---- prologue: the first segment's escape data, then its stage 0 ----
   SegGeo cur;
-  seg_setup(g, u_first, u_end, cur);
   SegEsc se;
-  load_seg_esc(g, rp, rbase, cur.rg, se);
+  const int64_t rg_first = (u_first / g.upt) / g.MT;
+  load_seg_esc(g, rp, rbase, rg_first, se);
   uint32_t s0, s1;
-  slice_range(g, cur.rg, se, s0, s1);   // waits for the loads above
+  slice_range(g, rg_first, se, s0, s1);   // waits for the loads above
+  seg_setup(g, u_first, u_end, (s1 - s0) <= (uint32_t)kSliceEntries, cur);
   issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
-  if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, 0, &xring0, wave);
-  else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo, cur.sl.c_lo < cur.sl.c_hi, xa0, xb0);
+  if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, 0, &xring0, wave);
+  else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
   issue_slice(re, s0, &slices[0][0], wave);
   wait_vmcnt<0>();
   barrier();
@@ -631,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     uint32_t lo, hi;
     seg_bounds(g, cur.rg, rb, se, lo, hi);
     bb2[rb] = base_pair(se.base[rb] ? se.base[rb] : 1u);
-    esc_start(cur_esc[rb], g, lo, hi, cur.sl.c_lo * kChunkK, in_lds, s0, slice_addr0);
+    esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, s0, slice_addr0);
   }
   int64_t pend0 = 0, pend1 = 0;   // tiles of the (at most two) partial segments
   int npend = 0;
@@ -656,8 +673,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       uint2 l[RB];
       if constexpr (Path::kXInLds) read_stage_wx<Path::kAcc>(ah, al, Path::x_addr(xs, wave), h, l, xa, xb);
       else read_stage_w(ah, al, h, l);
-      const uint32_t c = cur.sl.c_lo + j;
-      const bool valid = c < cur.sl.c_hi;
+      const uint32_t c = cur.sl.c0 + cur.sl.stride * j;
+      const bool valid = c < cur.sl.c_end;
       const uint32_t k0 = c * kChunkK;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -673,8 +690,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       int pend = 0;
       if (more1) {
         issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, j + 1, &xring1, wave);
-        else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo + j + 1, cur.sl.c_lo + j + 1 < cur.sl.c_hi, xa1, xb1);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
+        else {
+          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
+          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
+        }
         pend = V;
       }
       if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
@@ -688,8 +708,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       pend = 0;
       if (more2) {
         issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc_lo, cur.xc_hi, j + 2, &xring0, wave);
-        else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c_lo + j + 2, cur.sl.c_lo + j + 2 < cur.sl.c_hi, xa0, xb0);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 2, &xring0, wave);
+        else {
+          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
+          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa0, xb0);
+        }
         pend = V;
       }
       if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
@@ -708,13 +731,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
         slice_range(g, nrg, nse, ns0, ns1);
         issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
       }
-      seg_setup(g, cur.seg_end, u_end, nxt);
+      seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, nxt);
     }
     wait_vmcnt<0>();   // this wave's slice part (and any stage) has landed
     if (has_next) {
       issue_w<RB>(g, rh, rl, nxt.soff_h, nxt.sl, 0, &ring0, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nxt.xc_lo, nxt.xc_hi, 0, &xring0, wave);
-      else Path::load_x(g, rx, nxt.m0 * MROWS, nxt.sl.c_lo, nxt.sl.c_lo < nxt.sl.c_hi, xa0, xb0);
+      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nxt.xc0, nxt.xc_end, nxt.sl.stride, 0, &xring0, wave);
+      else Path::load_x(g, rx, nxt.m0 * MROWS, nxt.sl.c0, nxt.sl.c0 < nxt.sl.c_end, xa0, xb0);
     }
     // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
@@ -754,7 +777,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       uint32_t lo, hi;
       seg_bounds(g, cur.rg, rb, nse, lo, hi);
       bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
-      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c_lo * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
     }
   }
 
