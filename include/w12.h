@@ -127,7 +127,9 @@ int w12_unpack_records(const w12_tensor *t, uint16_t *rec, int64_t ldr, hipStrea
 
 /* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only.
  * The workspace starts with one 32-bit arrival counter per output tile (split-K
- * bookkeeping) followed by the FP32 slice partials. */
+ * bookkeeping) followed by the FP32 slice partials.  The size follows the plan, so a change
+ * of W12_GEMV_MAX_M between sizing and calling can make the workspace too small (reported as
+ * W12_ERR_WORKSPACE_TOO_SMALL). */
 int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
 
 /* Zero-fill a GEMM workspace of ws_bytes bytes on `stream`.  Call it once after allocating
@@ -141,8 +143,10 @@ int w12_gemm_workspace_init(void *ws, uint64_t ws_bytes, hipStream_t stream);
  * section 4.1: the GEMM decodes W12 records in registers and reduces in a fixed order).
  * X: BF16 [M][ldx]; Y: FP32 [M][ldy], every Y[m][n] (n < N) is written.  Accumulation is
  * FP32; the result is within 2^-12 * sum_k |x w| of the exact sum and bitwise identical
- * from run to run on the same device for the same (M, N, K).  M <= 8 runs a wavefront
- * GEMV, larger M runs bf16 MFMA tiles.  The K range may be split over several work-groups;
+ * from run to run on the same device for the same (M, N, K).  M <= 2 runs a wavefront
+ * GEMV (FP32 dot2 products and a fixed-order wavefront reduction), larger M runs bf16 MFMA
+ * tiles; the environment variable W12_GEMV_MAX_M (0..8, read at each call) moves that
+ * boundary.  The K range may be split over several work-groups;
  * the last one to finish a tile sums the slice partials in increasing slice order (no
  * floating-point atomics).  ws: device workspace of at least w12_gemm_workspace_size bytes,
  * initialised once with w12_gemm_workspace_init (only its counter region must be zero; the
@@ -153,7 +157,7 @@ int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
 
 /* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
-  int32_t path;              /* 1 = GEMV (M <= 8), 2 = MFMA                              */
+  int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles                       */
   int32_t splits;            /* K slices per output tile                                 */
   int32_t rows_per_block;    /* rows of W per work-group tile                            */
   int32_t m_tile;            /* rows of X per work-group tile                            */

@@ -935,9 +935,18 @@ static int groups_per_cu(int path, int M, int m_tile) {
   }
 }
 
+// Largest M that runs the wavefront GEMV; larger M runs MFMA tiles.  Both paths serve any
+// M <= 8.  Measured on MI355X at the dense-layer shapes, the GEMV is faster for M = 1 and 2
+// only: above that its per-row dot2 work grows with M while a 16-row MFMA tile costs the same
+// for every M <= 16.  W12_GEMV_MAX_M (0..8) moves the boundary, e.g. 8 for the wavefront
+// reduction at every M <= 8.
+constexpr int kGemvMaxM = 2;
+
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   GemmPlan p{};
-  p.path = (M <= 8) ? 1 : 2;
+  int gemv_max = env_int("W12_GEMV_MAX_M", kGemvMaxM);
+  gemv_max = gemv_max < 0 ? 0 : (gemv_max > 8 ? 8 : gemv_max);
+  p.path = (M <= gemv_max) ? 1 : 2;
   p.rb = kRB;
   p.waves = kWaves;
   const int64_t Nb = num_row_blocks(N);

@@ -118,7 +118,7 @@ def test_encode_decode_verify_validation():
                                    (512, 34816, 5120), (9, 1, 16), (3, 17, 33)])
 def test_gemm_plan_is_consistent(m, n, k):
     p = w12.gemm_plan(m, n, k)
-    assert p["path"] == (1 if m <= 8 else 2)
+    assert p["path"] == (1 if m <= 2 else 2)
     assert p["splits"] >= 1
     kc = (k + 15) // 16
     upt = (kc + 15) // 16                       # stream-K units (16 chunks) per tile
@@ -130,3 +130,14 @@ def test_gemm_plan_is_consistent(m, n, k):
     xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
     assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * 64 * p["m_tile"] * 4 + xpad
     assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]
+
+
+@pytest.mark.parametrize("limit", [0, 1, 5, 8, 99, -3])
+def test_gemm_gemv_boundary_env(monkeypatch, limit):
+    """W12_GEMV_MAX_M moves the GEMV / MFMA boundary (clamped to 0..8) at each call."""
+    monkeypatch.setenv("W12_GEMV_MAX_M", str(limit))
+    eff = min(max(limit, 0), 8)
+    for m in range(1, 17):
+        p = w12.gemm_plan(m, 4096, 4096)
+        assert p["path"] == (1 if m <= eff else 2), (limit, m)
+        assert p["m_tile"] == (m if p["path"] == 1 else 16)

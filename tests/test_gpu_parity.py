@@ -170,6 +170,20 @@ def test_gemm_within_tolerance(name, m):
     run_gemm_check(name, m)
 
 
+@pytest.mark.parametrize("name", GEMM_SHAPES)
+@pytest.mark.parametrize("limit,ms", [(8, [3, 4, 5, 6, 7, 8]), (0, [1, 2])])
+def test_gemm_other_path_within_tolerance(monkeypatch, name, limit, ms):
+    """Both inner products serve every M <= 8: the wavefront GEMV at M = 3..8 and the MFMA
+    tiles at M = 1, 2, selected with W12_GEMV_MAX_M."""
+    if name == "uniform_bits_100x520":
+        pytest.skip("random bit patterns overflow FP32 products; covered by encode/decode tests")
+    monkeypatch.setenv("W12_GEMV_MAX_M", str(limit))
+    w, _ = case(name)
+    for m in ms:
+        assert w12.gemm_plan(m, *w.shape)["path"] == (1 if limit else 2)
+        run_gemm_check(name, m, seed=1000)
+
+
 @pytest.mark.parametrize("m", [1, 4, 8, 16, 32, 64, 100])
 def test_gemm_bitwise_deterministic(m):
     """20 runs bitwise identical; the partial region of the workspace is NaN-poisoned before
