@@ -38,7 +38,8 @@
  *     written with vector accesses (W, X, decode output, verify reference) need a
  *     16-byte aligned base pointer and a pitch that is a multiple of 8 elements.
  *   - Shapes: 1 <= N <= 2^24, 1 <= K <= 65536 (k fits the 16-bit field of an escape
- *     entry), N*K < 2^32 (escape counts are 32-bit); 1 <= M <= 4096 for the GEMM.
+ *     entry), N*K < 2^32 (escape counts are 32-bit); 1 <= M <= 4096 for the GEMM, whose
+ *     X and Y must each span fewer than 2^29 elements ((M-1)*pitch + row length).
  */
 #ifndef W12_H
 #define W12_H

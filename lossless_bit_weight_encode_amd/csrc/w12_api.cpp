@@ -168,6 +168,8 @@ int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, flo
     return fail(W12_ERR_UNSUPPORTED_SHAPE, "X spans too many elements for 31-bit buffer offsets");
   if (!Y) return fail(W12_ERR_INVALID_ARG, "Y is NULL");
   if (ldy < t->N) return fail(W12_ERR_INVALID_ARG, "Y pitch %lld < N", (long long)ldy);
+  if (((int64_t)M - 1) * ldy + t->N >= (int64_t(1) << 29))
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "Y spans too many elements for 31-bit buffer offsets");
   if (!aligned(Y, 4)) return fail(W12_ERR_MISALIGNED, "Y must be 4-byte aligned");
   const w12::GemmPlan p = w12::plan_gemm(M, t->N, t->K);
   if (ws_bytes < p.ws_bytes)

@@ -36,7 +36,8 @@ constexpr int kSubRanges = kWaves * 4;
 constexpr int kUnitChunks = kSubRanges;   // chunks per stream-K unit (one per sub-range)
 constexpr int kRB = 4;                    // row blocks per tile (64 rows)
 constexpr int kTileRows = kRB * kRowsPerBlock;
-constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any plane: reads give 0
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any plane: reads give 0, writes are dropped
+constexpr int kCachePolicySc1 = 16;             // buffer access cache policy: sc1 (device coherent)
 
 __device__ __forceinline__ int64_t split_point(int64_t total, int64_t parts, int64_t q) { return q * total / parts; }
 __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -57,7 +58,7 @@ struct GemmArgs {
   int64_t upt;          // units per tile
   int64_t units;        // tiles x upt
   int64_t G;            // work-groups
-  uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes;
+  uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
   uint32_t* counters;   // [tiles]
@@ -240,9 +241,10 @@ struct SegLane {
   uint32_t lo_rb0, lo_rb1;             // lo plane offsets of the row blocks this lane copies
 };
 
+// Stage j of a segment into st; a stage that is not live (a padding step) reads nothing.
 template <int RB>
 __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
-                                        const uint32_t soff_h[RB], const SegLane& sl, uint32_t j,
+                                        const uint32_t soff_h[RB], const SegLane& sl, uint32_t j, bool live,
                                         RingStage<RB>* st, int wave) {
   const int lane = threadIdx.x & 63, r = lane & 15;
   const uint32_t c = sl.c0 + sl.stride * j;
@@ -251,11 +253,12 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
   // the compiler to prove it uniform, and it cannot once scalar registers run out
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16,
+                                             (int)(live ? soff_h[rb] + vh : kOutOfRange), 0, 0, 0);
   const uint32_t cd = sl.cd0 + sl.stride * j;
   const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
-  dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
-  if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
+  dma16(rl, &st->lo[wave][0], live ? sl.lo_rb0 + vl : kOutOfRange);
+  if (RB > 2) dma16(rl, &st->lo[wave][64], live ? sl.lo_rb1 + vl : kOutOfRange);
 }
 
 // Byte addresses (in LDS) of this lane's hi and lo slots of row block 0 of a stage.
@@ -578,13 +581,20 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t 
   }
 }
 
-// At most `pend` vector-memory instructions may remain outstanding (compile-time cases).
-template <int V>
+// At most `pend` vector-memory instructions may remain outstanding.  pend is a sum of: V (a
+// stage), 2 kRB (escape metadata), 1 (escape slice) and S (the previous segment's output
+// stores); any other value waits for everything.
+template <int V, int S>
 __device__ __forceinline__ void wait_pending(int pend) {
-  if (pend == V + 2 * kRB) wait_vmcnt<V + 2 * kRB>();
+  constexpr int E = 2 * kRB;
+  if (pend == S + V + E) wait_vmcnt<S + V + E>();
+  else if (pend == S + V) wait_vmcnt<S + V>();
+  else if (pend == S + E) wait_vmcnt<S + E>();
+  else if (pend == S) wait_vmcnt<S>();
+  else if (pend == V + E) wait_vmcnt<V + E>();
   else if (pend == V + 1) wait_vmcnt<V + 1>();
   else if (pend == V) wait_vmcnt<V>();
-  else if (pend == 2 * kRB) wait_vmcnt<2 * kRB>();
+  else if (pend == E) wait_vmcnt<E>();
   else if (pend == 1) wait_vmcnt<1>();
   else wait_vmcnt<0>();
 }
@@ -599,12 +609,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   constexpr int MROWS = Path::kMRows;
   constexpr int V = Path::kVmemPerStage;
   constexpr int TILE_ELEMS = ROWS * MROWS;
+  constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;   // output elements per thread
   typedef typename Path::XStage XStage;
   __shared__ RingStage<RB> ring0, ring1;
   __shared__ XStage xring0, xring1;
   __shared__ uint4 slices[2][kSliceEntries / 4];
   __shared__ float red[TILE_ELEMS];
-  __shared__ uint32_t s_flag;
+  __shared__ uint32_t s_flag[2];
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(g.lo, g.lo_bytes);
@@ -612,6 +623,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(g.esc_ptr, (uint32_t)(g.N + 1) * 4u);
   const __amdgpu_buffer_rsrc_t re = make_rsrc(g.esc, g.esc_bytes);
   const __amdgpu_buffer_rsrc_t rbase = make_rsrc(g.base, (uint32_t)g.N);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(g.Y, g.y_bytes);
+  const __amdgpu_buffer_rsrc_t rpart = make_rsrc(g.P, g.p_bytes);
 
   const int64_t u_first = ubeg(g, blockIdx.x);
   const int64_t u_end = ubeg(g, (int64_t)blockIdx.x + 1);
@@ -623,18 +636,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   const uint32_t slice_addr0 = lds_off(&slices[0][0]), slice_addr1 = lds_off(&slices[1][0]);
   const uint32_t red_addr = lds_off(&red[0]);
 
-  // ---- prologue: the first segment's escape data, then its stage 0 ----
+  // ---- prologue: stage 0 of the first segment (interleaved mapping assumed) alongside its
+  // escape metadata, then the escape slice ----
   SegGeo cur;
-  SegEsc se;
-  const int64_t rg_first = (u_first / g.upt) / g.MT;
-  load_seg_esc(g, rp, rbase, rg_first, se);
-  uint32_t s0, s1;
-  slice_range(g, rg_first, se, s0, s1);   // waits for the loads above
-  seg_setup(g, u_first, u_end, (s1 - s0) <= (uint32_t)kSliceEntries, cur);
-  issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
+  seg_setup(g, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
-  if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, 0, &xring0, wave);
-  else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
+  auto issue_stage0 = [&]() {
+    issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, true, &ring0, wave);
+    if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, 0, &xring0, wave);
+    else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
+  };
+  issue_stage0();
+  SegEsc se;
+  load_seg_esc(g, rp, rbase, cur.rg, se);
+  uint32_t s0, s1;
+  slice_range(g, cur.rg, se, s0, s1);   // waits for the loads above (and so for stage 0)
+  if ((s1 - s0) > (uint32_t)kSliceEntries) {
+    // escape lists too long for LDS: contiguous mapping; stage 0 again (the first copy has landed)
+    wait_vmcnt<0>();
+    seg_setup(g, u_first, u_end, false, cur);
+    issue_stage0();
+  }
   issue_slice(re, s0, &slices[0][0], wave);
   wait_vmcnt<0>();
   barrier();
@@ -652,22 +674,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   }
   int64_t pend0 = 0, pend1 = 0;   // tiles of the (at most two) partial segments
   int npend = 0;
+  int out_pend = 0;   // output stores issued after the current segment's stage 0
 
+  // Segments run back to back without draining the pipeline: a segment's steps are padded to
+  // an even count (a padding step reads nothing: its loads are out of range and give zeros,
+  // and its chunk is past every lane's range), so its last step is odd and fetches the next
+  // segment's stage 0 into ring0 / the even X registers, where every segment starts.
   for (;;) {
     const bool has_next = cur.seg_end < u_end;
     const int64_t nrg = has_next ? (cur.tile + 1) / g.MT : 0;
     SegEsc nse;
     uint32_t ns0 = 0, ns1 = 0;
-    bool next_sliced = false;
     typename Path::Acc acc[RB][Path::kAcc];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) Path::zero(acc[rb]);
     const uint32_t iters = cur.sl.iters;
-
+    const uint32_t iters2 = (iters + 1u) & ~1u;
     const uint32_t sl_addr = sb ? slice_addr1 : slice_addr0;
+
     // stage j is complete once at most `pend` newer vector-memory instructions remain
     auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
-      wait_pending<V>(pend);
+      wait_pending<V, ET>(pend);
       static_assert(RB == 4, "ring reads are written for 4 row blocks");
       uint4 h[RB];
       uint2 l[RB];
@@ -684,30 +711,26 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
         Path::mac(d, xa, xb, acc[rb]);
       }
     };
-    for (uint32_t j = 0; j < iters; j += 2) {
-      // even step: stage j in ring0
-      const bool more1 = j + 1 < iters;
-      int pend = 0;
-      if (more1) {
-        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
-        else {
-          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
-          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
-        }
-        pend = V;
+    for (uint32_t j = 0; j < iters2; j += 2) {
+      // even step: stage j in ring0; fetch stage j + 1 (always inside the padded count)
+      issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, j + 1 < iters, &ring1, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
+      else {
+        const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
+        Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
       }
+      int pend = V;
       if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
         load_seg_esc(g, rp, rbase, nrg, nse);
         pend += 2 * RB;
       }
+      if (j == 0) pend += out_pend;
       compute(ah0, al0, &xring0, xa0, xb0, j, pend);
-      if (!more1) break;
-      // odd step: stage j + 1 in ring1
-      const bool more2 = j + 2 < iters;
+      // odd step: stage j + 1 in ring1; fetch stage j + 2, or the next segment's stage 0
       pend = 0;
-      if (more2) {
-        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
+      const bool last = j + 2 >= iters2;
+      if (!last) {
+        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, j + 2 < iters, &ring0, wave);
         if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 2, &xring0, wave);
         else {
           const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
@@ -718,27 +741,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
         slice_range(g, nrg, nse, ns0, ns1);
         issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
-        next_sliced = true;
         pend += 1;
+      }
+      if (last && has_next) {
+        // the next segment's geometry is recomputed where it is needed (short live ranges)
+        SegGeo nx;
+        seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+        issue_w<RB>(g, rh, rl, nx.soff_h, nx.sl, 0, true, &ring0, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, 0, &xring0, wave);
+        else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
+        pend += V;
       }
       compute(ah1, al1, &xring1, xa1, xb1, j + 1, pend);
     }
 
-    // ---- segment end: the next segment's escape slice and stage 0, then the epilogue ----
-    SegGeo nxt;
-    if (has_next) {
-      if (!next_sliced) {
-        slice_range(g, nrg, nse, ns0, ns1);
-        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
-      }
-      seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, nxt);
-    }
-    wait_vmcnt<0>();   // this wave's slice part (and any stage) has landed
-    if (has_next) {
-      issue_w<RB>(g, rh, rl, nxt.soff_h, nxt.sl, 0, &ring0, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nxt.xc0, nxt.xc_end, nxt.sl.stride, 0, &xring0, wave);
-      else Path::load_x(g, rx, nxt.m0 * MROWS, nxt.sl.c0, nxt.sl.c0 < nxt.sl.c_end, xa0, xb0);
-    }
+    // ---- segment end ----
+    // this wave's part of the next slice (issued before the next stage 0) has landed
+    if (has_next) wait_vmcnt<V>();
     // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
       if (wave == w) Path::to_red(acc, red_addr, w == 0);
@@ -748,18 +767,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
     const int m0 = cur.m0 * MROWS;
     const int pos = (cur.u == u_first) ? 0 : 1;   // partial slot: the work-group's first or last segment
-    float* mine = g.P + (2 * (int64_t)blockIdx.x + pos) * (int64_t)TILE_ELEMS;
-    // red, the partial tiles and Y's rows share the order e = m * 64 + row: consecutive threads
-    // touch consecutive channels
-    for (int e = threadIdx.x; e < TILE_ELEMS; e += kThreads) {
-      const float v = __builtin_bit_cast(float, lds_read_u32(red_addr + (uint32_t)(e * 4)));
+    const uint32_t slot = (uint32_t)((2 * (int64_t)blockIdx.x + pos) * TILE_ELEMS);
+    // exactly ET buffer stores per thread (out-of-range offsets are dropped), so the next
+    // segment's first wait can leave them in flight.  red, the partial tiles and Y's rows share
+    // the order e = m * 64 + row: consecutive threads touch consecutive channels.
+#pragma unroll
+    for (int i = 0; i < ET; ++i) {
+      const int e = (int)threadIdx.x + i * kThreads;
+      const bool in_tile = (TILE_ELEMS % kThreads == 0) || e < TILE_ELEMS;
+      const uint32_t v = lds_read_u32(red_addr + (uint32_t)((in_tile ? e : 0) * 4));
       if (full) {
         const int row = e % ROWS, ml = e / ROWS;
         const int64_t n = cur.rg * ROWS + row;
         const int m = m0 + ml;
-        if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v;
+        const uint32_t off = (in_tile && n < g.N && m < g.M) ? (uint32_t)(((int64_t)m * g.ldy + n) * 4) : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(v, ry, (int)off, 0, 0);
       } else {
-        __hip_atomic_store(mine + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // device-coherent (sc1) store: the tile's last arriver may run on another XCD
+        const uint32_t off = in_tile ? (slot + (uint32_t)e) * 4u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(v, rpart, (int)off, 0, kCachePolicySc1);
       }
     }
     if (!full) {
@@ -769,7 +795,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     if (!has_next) break;
     barrier();   // red is free again; the next slice is visible to every wave
     // switch to the next segment
-    cur = nxt;
+    seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
     sb ^= 1;
     in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
 #pragma unroll
@@ -779,23 +805,30 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
       esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
     }
+    out_pend = ET;
   }
 
-  // ---- deferred split-K: bump the counters of partial tiles; the last arriver sums ----
+  // ---- deferred split-K: bump the counters of partial tiles (both at once); the last
+  // arriver of a tile sums it ----
   wait_vm_all();
+  __syncthreads();
+  if (npend == 0) return;
+  if (threadIdx.x < (unsigned)npend) {
+    const int64_t tile = threadIdx.x == 0 ? pend0 : pend1;
+    const int64_t t0 = tile * g.upt;
+    const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
+    const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
+    const uint32_t nsegs = (uint32_t)(w_b - w_a + 1);
+    const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
+  }
   __syncthreads();
   for (int p = 0; p < npend; ++p) {
     const int64_t tile = p == 0 ? pend0 : pend1;
     const int64_t t0 = tile * g.upt;
     const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
     const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
-    const uint32_t nsegs = (uint32_t)(w_b - w_a + 1);
-    if (threadIdx.x == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_flag = (prev == nsegs - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_flag) {
+    if (s_flag[p]) {
       const int64_t rg = tile / g.MT;
       const int m0 = (int)(tile - rg * g.MT) * MROWS;
       // the tile is the first segment of every contributor except possibly w_a
@@ -843,7 +876,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       }
       if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
   }
 }
 
@@ -922,13 +954,13 @@ static int groups_per_cu(int path, int M, int m_tile) {
       case 3: return occupancy_of<GemvPath<3>>(2);
       case 4: return occupancy_of<GemvPath<4>>(2);
       case 5: return occupancy_of<GemvPath<5>>(2);
-      case 6: return occupancy_of<GemvPath<6>>(2);
-      case 7: return occupancy_of<GemvPath<7>>(2);
-      default: return occupancy_of<GemvPath<8>>(2);
+      case 6: return occupancy_of<GemvPath<6>>(1);
+      case 7: return occupancy_of<GemvPath<7>>(1);
+      default: return occupancy_of<GemvPath<8>>(1);
     }
   }
   switch (m_tile / 16) {
-    case 1: return occupancy_of<MfmaPath<1>>(3);
+    case 1: return occupancy_of<MfmaPath<1>>(2);
     case 2: return occupancy_of<MfmaPath<2>>(2);
     case 3: return occupancy_of<MfmaPath<3>>(1);
     default: return occupancy_of<MfmaPath<4>>(1);
@@ -966,6 +998,14 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", groups_per_cu(p.path, M, p.m_tile));
   if (G > p.units) G = p.units;
   if (G < 1) G = 1;
+  // When the tiles fit in the resident work-groups, use a whole multiple of them (keeping at
+  // least 3/4 of the slots): every work-group then stays inside one tile, with one segment
+  // and at most one partial.  A work-group whose range crosses a tile boundary pays a second
+  // epilogue, a second partial and a second fixup, and the grid waits for the slowest one.
+  if (p.tiles <= G) {
+    const int64_t s = G / p.tiles;
+    if (4 * p.tiles * s >= 3 * G) G = p.tiles * s;
+  }
   p.grid = G;
   // segments per tile (1 when every work-group covers whole tiles)
   p.splits = (int)((p.upt * G + p.units - 1) / p.units);
@@ -1051,8 +1091,10 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   a.esc_bytes = (uint32_t)((uint64_t)t->num_escapes * 4u);
   a.Y = Y;
   a.ldy = ldy;
+  a.y_bytes = (uint32_t)((((uint64_t)M - 1) * (uint64_t)ldy + (uint64_t)t->N) * 4u);
   a.counters = reinterpret_cast<uint32_t*>(ws);
   a.P = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes);
+  a.p_bytes = (uint32_t)p.partial_bytes;
   dispatch(p, a, stream);
   return hipGetLastError();
 }
