@@ -147,7 +147,7 @@ int w12_gemm_workspace_init(void *ws, uint64_t ws_bytes, hipStream_t stream);
  * from run to run on the same device for the same (M, N, K).  M <= 2 runs a wavefront
  * GEMV (FP32 dot2 products and a fixed-order wavefront reduction), larger M runs bf16 MFMA
  * tiles; the environment variable W12_GEMV_MAX_M (0..8, read at each call) moves that
- * boundary.  The K range may be split over several work-groups;
+ * boundary, and W12_MAX_GRID (read at each call) caps the number of work-groups.  The K range may be split over several work-groups;
  * the last one to finish a tile sums the slice partials in increasing slice order (no
  * floating-point atomics).  ws: device workspace of at least w12_gemm_workspace_size bytes,
  * initialised once with w12_gemm_workspace_init (only its counter region must be zero; the

@@ -61,8 +61,8 @@ struct GemmArgs {
   uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
-  uint32_t* counters;   // [tiles]
-  float* P;             // [2G][tile elements]
+  uint32_t* counters;   // [tiles] arrival counters
+  float* P;             // [2G][tile elements] partial tiles
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -241,10 +241,10 @@ struct SegLane {
   uint32_t lo_rb0, lo_rb1;             // lo plane offsets of the row blocks this lane copies
 };
 
-// Stage j of a segment into st; a stage that is not live (a padding step) reads nothing.
+// Stage j of a segment into st.
 template <int RB>
 __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
-                                        const uint32_t soff_h[RB], const SegLane& sl, uint32_t j, bool live,
+                                        const uint32_t soff_h[RB], const SegLane& sl, uint32_t j,
                                         RingStage<RB>* st, int wave) {
   const int lane = threadIdx.x & 63, r = lane & 15;
   const uint32_t c = sl.c0 + sl.stride * j;
@@ -253,12 +253,11 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
   // the compiler to prove it uniform, and it cannot once scalar registers run out
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16,
-                                             (int)(live ? soff_h[rb] + vh : kOutOfRange), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
   const uint32_t cd = sl.cd0 + sl.stride * j;
   const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
-  dma16(rl, &st->lo[wave][0], live ? sl.lo_rb0 + vl : kOutOfRange);
-  if (RB > 2) dma16(rl, &st->lo[wave][64], live ? sl.lo_rb1 + vl : kOutOfRange);
+  dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
+  if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
 }
 
 // Byte addresses (in LDS) of this lane's hi and lo slots of row block 0 of a stage.
@@ -277,6 +276,7 @@ __device__ __forceinline__ void ring_addr(const RingStage<RB>* st, int wave, uin
 template <int M>
 struct GemvPath {
   static constexpr int kMRows = M;
+  static constexpr int kWavesPerEU = 2;   // register budget: two work-groups per CU
   static constexpr bool kXInLds = true;
   static constexpr int kVmemPerStage = 7;   // 6 W DMA + 1 X DMA
   typedef float Acc;
@@ -349,6 +349,7 @@ struct GemvPath {
 template <int MB>
 struct MfmaPath {
   static constexpr int kMRows = MB * 16;
+  static constexpr int kWavesPerEU = MB <= 2 ? 2 : 1;   // register budget: two work-groups per CU up to 32 rows
   static constexpr bool kXInLds = false;
   static constexpr int kVmemPerStage = 6 + 2 * MB;   // 6 W DMA + X loads
   typedef f32x4 Acc;
@@ -437,6 +438,7 @@ __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w
 // its channel's part of it.  A larger slice (dense escapes) is walked in global memory.
 // ------------------------------------------------------------------------------------------
 constexpr int kSliceEntries = kWaves * kWave * 4;   // 1024
+constexpr int kMaxPend = 2;   // partial tiles of a work-group: its first and last segment
 
 struct SegEsc {        // per lane, loaded one segment ahead
   uint2 ptr[kRB];      // {esc_ptr[n], esc_ptr[n + 1]} of the lane's 4 channels
@@ -581,17 +583,13 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t 
   }
 }
 
-// At most `pend` vector-memory instructions may remain outstanding.  pend is a sum of: V (a
-// stage), 2 kRB (escape metadata), 1 (escape slice) and S (the previous segment's output
-// stores); any other value waits for everything.
-template <int V, int S>
+// At most `pend` vector-memory instructions may remain outstanding.  pend counts loads only
+// (a stage: V, escape metadata: 2 kRB, the escape slice: 1); any other value waits for
+// everything.  Leaving an instruction out of the count only makes the wait longer.
+template <int V>
 __device__ __forceinline__ void wait_pending(int pend) {
   constexpr int E = 2 * kRB;
-  if (pend == S + V + E) wait_vmcnt<S + V + E>();
-  else if (pend == S + V) wait_vmcnt<S + V>();
-  else if (pend == S + E) wait_vmcnt<S + E>();
-  else if (pend == S) wait_vmcnt<S>();
-  else if (pend == V + E) wait_vmcnt<V + E>();
+  if (pend == V + E) wait_vmcnt<V + E>();
   else if (pend == V + 1) wait_vmcnt<V + 1>();
   else if (pend == V) wait_vmcnt<V>();
   else if (pend == E) wait_vmcnt<E>();
@@ -603,7 +601,8 @@ __device__ __forceinline__ void wait_pending(int pend) {
 // The kernel.
 // ------------------------------------------------------------------------------------------
 template <class Path>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
+void k_gemm(GemmArgs g) {
   constexpr int RB = kRB;
   constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
@@ -615,7 +614,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   __shared__ XStage xring0, xring1;
   __shared__ uint4 slices[2][kSliceEntries / 4];
   __shared__ float red[TILE_ELEMS];
-  __shared__ uint32_t s_flag[2];
+  __shared__ uint32_t s_flag[kMaxPend];
+  __shared__ uint32_t s_pend[kMaxPend];   // tiles of this work-group's partial segments
   const int wave = wave_id();
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(g.lo, g.lo_bytes);
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
   seg_setup(g, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
   auto issue_stage0 = [&]() {
-    issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, true, &ring0, wave);
+    issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
     if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, 0, &xring0, wave);
     else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
   };
@@ -672,172 +672,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
     bb2[rb] = base_pair(se.base[rb] ? se.base[rb] : 1u);
     esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, s0, slice_addr0);
   }
-  int64_t pend0 = 0, pend1 = 0;   // tiles of the (at most two) partial segments
-  int npend = 0;
-  int out_pend = 0;   // output stores issued after the current segment's stage 0
+  int npend = 0;   // partial tiles listed in s_pend (the first and last segment at most)
 
-  // Segments run back to back without draining the pipeline: a segment's steps are padded to
-  // an even count (a padding step reads nothing: its loads are out of range and give zeros,
-  // and its chunk is past every lane's range), so its last step is odd and fetches the next
-  // segment's stage 0 into ring0 / the even X registers, where every segment starts.
-  for (;;) {
-    const bool has_next = cur.seg_end < u_end;
-    const int64_t nrg = has_next ? (cur.tile + 1) / g.MT : 0;
-    SegEsc nse;
-    uint32_t ns0 = 0, ns1 = 0;
-    typename Path::Acc acc[RB][Path::kAcc];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) Path::zero(acc[rb]);
-    const uint32_t iters = cur.sl.iters;
-    const uint32_t iters2 = (iters + 1u) & ~1u;
-    const uint32_t sl_addr = sb ? slice_addr1 : slice_addr0;
-
-    // stage j is complete once at most `pend` newer vector-memory instructions remain
-    auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
-      wait_pending<V, ET>(pend);
-      static_assert(RB == 4, "ring reads are written for 4 row blocks");
-      uint4 h[RB];
-      uint2 l[RB];
-      if constexpr (Path::kXInLds) read_stage_wx<Path::kAcc>(ah, al, Path::x_addr(xs, wave), h, l, xa, xb);
-      else read_stage_w(ah, al, h, l);
-      const uint32_t c = cur.sl.c0 + cur.sl.stride * j;
-      const bool valid = c < cur.sl.c_end;
-      const uint32_t k0 = c * kChunkK;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        uint32_t d[8];
-        decode16(h[rb], l[rb], bb2[rb], d);
-        if (valid) esc_apply(cur_esc[rb], g.esc, k0, d, in_lds, sl_addr);
-        Path::mac(d, xa, xb, acc[rb]);
-      }
-    };
-    for (uint32_t j = 0; j < iters2; j += 2) {
-      // even step: stage j in ring0; fetch stage j + 1 (always inside the padded count)
-      issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, j + 1 < iters, &ring1, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
-      else {
-        const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
-        Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
-      }
-      int pend = V;
-      if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
-        load_seg_esc(g, rp, rbase, nrg, nse);
-        pend += 2 * RB;
-      }
-      if (j == 0) pend += out_pend;
-      compute(ah0, al0, &xring0, xa0, xb0, j, pend);
-      // odd step: stage j + 1 in ring1; fetch stage j + 2, or the next segment's stage 0
-      pend = 0;
-      const bool last = j + 2 >= iters2;
-      if (!last) {
-        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, j + 2 < iters, &ring0, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 2, &xring0, wave);
-        else {
-          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
-          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa0, xb0);
-        }
-        pend = V;
-      }
-      if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
-        slice_range(g, nrg, nse, ns0, ns1);
-        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
-        pend += 1;
-      }
-      if (last && has_next) {
-        // the next segment's geometry is recomputed where it is needed (short live ranges)
-        SegGeo nx;
-        seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
-        issue_w<RB>(g, rh, rl, nx.soff_h, nx.sl, 0, true, &ring0, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, 0, &xring0, wave);
-        else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
-        pend += V;
-      }
-      compute(ah1, al1, &xring1, xa1, xb1, j + 1, pend);
+  // The counters of the listed partial tiles go up together (one round trip); the last
+  // arriver of a tile sums its partials in work-group order and writes Y.  A tile has one
+  // partial slot per work-group range that meets it (that work-group's first or last segment).
+  auto flush_pending = [&]() {
+    wait_vm_all();   // this work-group's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x < (unsigned)npend) {
+      const int64_t tile = s_pend[threadIdx.x];
+      const int64_t t0 = tile * g.upt;
+      const uint32_t nsegs = (uint32_t)(ceil_div((t0 + g.upt) * g.G, g.units) - ceil_div((t0 + 1) * g.G, g.units) + 1);
+      const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
     }
-
-    // ---- segment end ----
-    // this wave's part of the next slice (issued before the next stage 0) has landed
-    if (has_next) wait_vmcnt<V>();
-    // waves add their partial tiles into red in wave order
-    for (int w = 0; w < kWaves; ++w) {
-      if (wave == w) Path::to_red(acc, red_addr, w == 0);
-      wait_lgkm();
-      barrier();
-    }
-    const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
-    const int m0 = cur.m0 * MROWS;
-    const int pos = (cur.u == u_first) ? 0 : 1;   // partial slot: the work-group's first or last segment
-    const uint32_t slot = (uint32_t)((2 * (int64_t)blockIdx.x + pos) * TILE_ELEMS);
-    // exactly ET buffer stores per thread (out-of-range offsets are dropped), so the next
-    // segment's first wait can leave them in flight.  red, the partial tiles and Y's rows share
-    // the order e = m * 64 + row: consecutive threads touch consecutive channels.
-#pragma unroll
-    for (int i = 0; i < ET; ++i) {
-      const int e = (int)threadIdx.x + i * kThreads;
-      const bool in_tile = (TILE_ELEMS % kThreads == 0) || e < TILE_ELEMS;
-      const uint32_t v = lds_read_u32(red_addr + (uint32_t)((in_tile ? e : 0) * 4));
-      if (full) {
-        const int row = e % ROWS, ml = e / ROWS;
-        const int64_t n = cur.rg * ROWS + row;
-        const int m = m0 + ml;
-        const uint32_t off = (in_tile && n < g.N && m < g.M) ? (uint32_t)(((int64_t)m * g.ldy + n) * 4) : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b32(v, ry, (int)off, 0, 0);
-      } else {
-        // device-coherent (sc1) store: the tile's last arriver may run on another XCD
-        const uint32_t off = in_tile ? (slot + (uint32_t)e) * 4u : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b32(v, rpart, (int)off, 0, kCachePolicySc1);
-      }
-    }
-    if (!full) {
-      if (npend == 0) pend0 = cur.tile; else pend1 = cur.tile;
-      ++npend;
-    }
-    if (!has_next) break;
-    barrier();   // red is free again; the next slice is visible to every wave
-    // switch to the next segment
-    seg_setup(g, cur.seg_end, u_end, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
-    sb ^= 1;
-    in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      uint32_t lo, hi;
-      seg_bounds(g, cur.rg, rb, nse, lo, hi);
-      bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
-      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
-    }
-    out_pend = ET;
-  }
-
-  // ---- deferred split-K: bump the counters of partial tiles (both at once); the last
-  // arriver of a tile sums it ----
-  wait_vm_all();
-  __syncthreads();
-  if (npend == 0) return;
-  if (threadIdx.x < (unsigned)npend) {
-    const int64_t tile = threadIdx.x == 0 ? pend0 : pend1;
-    const int64_t t0 = tile * g.upt;
-    const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
-    const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
-    const uint32_t nsegs = (uint32_t)(w_b - w_a + 1);
-    const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  for (int p = 0; p < npend; ++p) {
-    const int64_t tile = p == 0 ? pend0 : pend1;
-    const int64_t t0 = tile * g.upt;
-    const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
-    const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
-    if (s_flag[p]) {
-      const int64_t rg = tile / g.MT;
-      const int m0 = (int)(tile - rg * g.MT) * MROWS;
+    __syncthreads();
+    for (int p = 0; p < npend; ++p) {
+      if (!s_flag[p]) continue;
+      const int64_t tile = s_pend[p];
+      const int64_t t0 = tile * g.upt;
+      const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
+      const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
+      const int64_t ns = w_b - w_a + 1;
       // the tile is the first segment of every contributor except possibly w_a
       const int pos_a = ubeg(g, w_a) < t0 ? 1 : 0;
-      // every load of a batch (up to 64 per thread: KB <= 16 contributors x ET elements) is issued
+      auto slot_of = [&](int64_t j) -> int64_t { return 2 * (w_a + j) + (j == 0 ? pos_a : 0); };
+      const int64_t rg = tile / g.MT;
+      const int m0 = (int)(tile - rg * g.MT) * MROWS;
+      // every load of a batch (up to 64 per thread: KB <= 16 slots x ET elements) is issued
       // before any is summed; the sum still runs in work-group order
-      constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;
       constexpr int KB = ET >= 64 ? 1 : (64 / ET < 16 ? 64 / ET : 16);
-      const int64_t ns = w_b - w_a + 1;
       float v[ET];
 #pragma unroll
       for (int k = 0; k < ET; ++k) v[k] = 0.f;
@@ -846,9 +711,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int sg = 0; sg < KB; ++sg) {
           if (b0 + sg < ns) {
-            const int64_t wj = w_a + b0 + sg;
-            const int pos = wj == w_a ? pos_a : 0;
-            const float* src = g.P + (2 * wj + pos) * (int64_t)TILE_ELEMS;
+            const float* src = g.P + slot_of(b0 + sg) * (int64_t)TILE_ELEMS;
 #pragma unroll
             for (int k = 0; k < ET; ++k) {
               const int e = (int)threadIdx.x + k * kThreads;
@@ -876,7 +739,149 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g) {
       }
       if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  };
+
+  // Every segment starts in ring0 / the even X registers: its stage 0 is fetched after the
+  // previous segment's last step, once that step's stage is no longer read.  Its fetch follows
+  // the previous segment's output stores, so no store is ever among the instructions a stage
+  // wait looks past (stores and loads may complete out of order on the shared counter).
+  for (;;) {
+    // the next segment: the rest of the range
+    const int64_t nu0 = cur.seg_end, nu1 = u_end;
+    const bool has_next = nu0 < nu1;
+    const int64_t nrg = has_next ? (nu0 / g.upt) / g.MT : 0;
+    SegEsc nse;
+    uint32_t ns0 = 0, ns1 = 0;
+    typename Path::Acc acc[RB][Path::kAcc];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) Path::zero(acc[rb]);
+    bool next_sliced = false;
+    const uint32_t iters = cur.sl.iters;
+    const uint32_t sl_addr = sb ? slice_addr1 : slice_addr0;
+
+    // stage j is complete once at most `pend` newer vector-memory instructions remain
+    auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
+      wait_pending<V>(pend);
+      static_assert(RB == 4, "ring reads are written for 4 row blocks");
+      uint4 h[RB];
+      uint2 l[RB];
+      if constexpr (Path::kXInLds) read_stage_wx<Path::kAcc>(ah, al, Path::x_addr(xs, wave), h, l, xa, xb);
+      else read_stage_w(ah, al, h, l);
+      const uint32_t c = cur.sl.c0 + cur.sl.stride * j;
+      const bool valid = c < cur.sl.c_end;
+      const uint32_t k0 = c * kChunkK;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        uint32_t d[8];
+        decode16(h[rb], l[rb], bb2[rb], d);
+        if (valid) esc_apply(cur_esc[rb], g.esc, k0, d, in_lds, sl_addr);
+        Path::mac(d, xa, xb, acc[rb]);
+      }
+    };
+    for (uint32_t j = 0; j < iters; j += 2) {
+      // even step: stage j in ring0
+      const bool more1 = j + 1 < iters;
+      int pend = 0;
+      if (more1) {
+        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
+        else {
+          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
+          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
+        }
+        pend = V;
+      }
+      if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
+        load_seg_esc(g, rp, rbase, nrg, nse);
+        pend += 2 * RB;
+      }
+      compute(ah0, al0, &xring0, xa0, xb0, j, pend);
+      if (!more1) break;
+      // odd step: stage j + 1 in ring1
+      const bool more2 = j + 2 < iters;
+      pend = 0;
+      if (more2) {
+        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 2, &xring0, wave);
+        else {
+          const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
+          Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa0, xb0);
+        }
+        pend = V;
+      }
+      if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
+        slice_range(g, nrg, nse, ns0, ns1);
+        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+        next_sliced = true;
+        pend += 1;
+      }
+      compute(ah1, al1, &xring1, xa1, xb1, j + 1, pend);
+    }
+
+    // ---- segment end ----
+    if (has_next && !next_sliced) {   // a one-step segment
+      slice_range(g, nrg, nse, ns0, ns1);
+      issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+    }
+    wait_vmcnt<0>();   // this wave's part of the next slice has landed
+    // waves add their partial tiles into red in wave order
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave == w) Path::to_red(acc, red_addr, w == 0);
+      wait_lgkm();
+      barrier();
+    }
+    const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
+    const int m0 = cur.m0 * MROWS;
+    // partial slot: the work-group's first or last segment
+    const int64_t slot_i = 2 * (int64_t)blockIdx.x + ((cur.u == u_first) ? 0 : 1);
+    const uint32_t slot = (uint32_t)(slot_i * TILE_ELEMS);
+    // buffer stores (out-of-range offsets are dropped).  red, the partial tiles and Y's rows
+    // share the order e = m * 64 + row: consecutive threads touch consecutive channels.
+#pragma unroll
+    for (int i = 0; i < ET; ++i) {
+      const int e = (int)threadIdx.x + i * kThreads;
+      const bool in_tile = (TILE_ELEMS % kThreads == 0) || e < TILE_ELEMS;
+      const uint32_t v = lds_read_u32(red_addr + (uint32_t)((in_tile ? e : 0) * 4));
+      if (full) {
+        const int row = e % ROWS, ml = e / ROWS;
+        const int64_t n = cur.rg * ROWS + row;
+        const int m = m0 + ml;
+        const uint32_t off = (in_tile && n < g.N && m < g.M) ? (uint32_t)(((int64_t)m * g.ldy + n) * 4) : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(v, ry, (int)off, 0, 0);
+      } else {
+        // device-coherent (sc1) store: the tile's last arriver may run on another XCD
+        const uint32_t off = in_tile ? (slot + (uint32_t)e) * 4u : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b32(v, rpart, (int)off, 0, kCachePolicySc1);
+      }
+    }
+    if (!full) {
+      if (threadIdx.x == 0) s_pend[npend] = (uint32_t)cur.tile;   // read after a barrier
+      ++npend;
+    }
+    if (!has_next) break;
+    {
+      SegGeo nx;
+      seg_setup(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+      issue_w<RB>(g, rh, rl, nx.soff_h, nx.sl, 0, &ring0, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, 0, &xring0, wave);
+      else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
+    }
+    barrier();   // red is free again; the next slice is visible to every wave
+    // switch to the next segment
+    seg_setup(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
+    sb ^= 1;
+    in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t lo, hi;
+      seg_bounds(g, cur.rg, rb, nse, lo, hi);
+      bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
+      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+    }
   }
+
+  // ---- deferred split-K fixups ----
+  if (npend) flush_pending();
 }
 
 __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
@@ -918,9 +923,6 @@ static int device_cus() {
   return cus;
 }
 
-template <class Path>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs g);
-
 // Resident work-groups per CU of one kernel variant, from the runtime occupancy calculator
 // (registers and LDS of the compiled kernel); when no device is visible, a conservative
 // estimate.  Cached per variant.
@@ -954,9 +956,9 @@ static int groups_per_cu(int path, int M, int m_tile) {
       case 3: return occupancy_of<GemvPath<3>>(2);
       case 4: return occupancy_of<GemvPath<4>>(2);
       case 5: return occupancy_of<GemvPath<5>>(2);
-      case 6: return occupancy_of<GemvPath<6>>(1);
-      case 7: return occupancy_of<GemvPath<7>>(1);
-      default: return occupancy_of<GemvPath<8>>(1);
+      case 6: return occupancy_of<GemvPath<6>>(2);
+      case 7: return occupancy_of<GemvPath<7>>(2);
+      default: return occupancy_of<GemvPath<8>>(2);
     }
   }
   switch (m_tile / 16) {
@@ -996,6 +998,8 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   p.upt = (Kc + kUnitChunks - 1) / kUnitChunks;
   p.units = p.tiles * p.upt;
   int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", groups_per_cu(p.path, M, p.m_tile));
+  const int max_grid = env_int("W12_MAX_GRID", 0);   // 0: no cap
+  if (max_grid > 0 && G > max_grid) G = max_grid;
   if (G > p.units) G = p.units;
   if (G < 1) G = 1;
   // When the tiles fit in the resident work-groups, use a whole multiple of them (keeping at

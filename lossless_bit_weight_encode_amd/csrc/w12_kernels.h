@@ -19,8 +19,8 @@ hipError_t launch_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, 
 hipError_t launch_unpack(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStream_t stream);
 
 struct GemmPlan {
-  int path;            // 1 = GEMV (M <= 8), 2 = MFMA
-  int splits;          // work-group segments per tile (1 when work-groups cover whole tiles)
+  int path;            // 1 = wavefront GEMV, 2 = MFMA tiles
+  int splits;          // partial sums per tile (1 when a tile is never split)
   int rb;              // row blocks of 16 per tile
   int waves;           // waves per work-group (they split a segment's K range)
   int m_tile;          // rows of X per tile
@@ -29,7 +29,7 @@ struct GemmPlan {
   int64_t tiles;       // row_groups * m_tiles
   int64_t upt;         // stream-K units (16 chunks) per tile
   int64_t units;       // tiles * upt
-  int64_t grid;        // work-groups G (resident at once; each takes units / G units)
+  int64_t grid;        // work-groups G (resident at once); w takes units [w U / G, (w+1) U / G)
   uint64_t counter_bytes;  // per-tile arrival counters at the start of the workspace
   uint64_t partial_bytes;  // two partial tiles per work-group
   uint64_t xpad_bytes;     // X padded to whole 16-k chunks (only when K % 16 != 0)

@@ -125,6 +125,9 @@ def test_gemm_plan_is_consistent(m, n, k):
     tiles = ((n + 15) // 16 + 3) // 4 * ((m + p["m_tile"] - 1) // p["m_tile"])
     assert 1 <= p["grid"] <= tiles * upt       # never more work-groups than units
     assert p["counter_bytes"] % 256 == 0 and p["counter_bytes"] >= 4 * tiles
+    if tiles <= p["grid"]:
+        # a whole multiple of the tiles when that keeps 3/4 of the grid: no range crosses a tile
+        assert p["grid"] % tiles == 0 or p["grid"] * 3 > 4 * (p["grid"] // tiles) * tiles
     # counters + two partial tiles (64 rows x m tile) per work-group (+ X padded to whole
     # 16-k chunks when K is ragged)
     xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
@@ -141,3 +144,13 @@ def test_gemm_gemv_boundary_env(monkeypatch, limit):
         p = w12.gemm_plan(m, 4096, 4096)
         assert p["path"] == (1 if m <= eff else 2), (limit, m)
         assert p["m_tile"] == (m if p["path"] == 1 else 16)
+
+
+@pytest.mark.parametrize("cap", [1, 3, 100])
+def test_gemm_grid_cap_env(monkeypatch, cap):
+    """W12_MAX_GRID caps the work-groups of a GEMM (read at each call)."""
+    monkeypatch.setenv("W12_MAX_GRID", str(cap))
+    for m, n, k in [(1, 5120, 5120), (16, 34816, 5120), (64, 300, 4096)]:
+        p = w12.gemm_plan(m, n, k)
+        assert 1 <= p["grid"] <= cap
+        assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]

@@ -207,6 +207,36 @@ def test_gemm_bitwise_deterministic(m):
     assert bad == 0
 
 
+@pytest.mark.parametrize("name,m,grid", [("gauss_300x4096", 1, 4), ("gauss_300x4096", 16, 3),
+                                         ("heavy_64x2048", 100, 1), ("wide_37x1000", 100, 1),
+                                         ("tiny_256x512", 64, 3), ("ragged_17x33", 70, 1)])
+def test_gemm_small_grid(monkeypatch, name, m, grid):
+    """More tiles than work-groups (the grid capped with W12_MAX_GRID): work-group ranges span
+    several tiles, with partial first and last segments and whole tiles between them.  Y is
+    bitwise identical from run to run and within tolerance, and the arrival counters are back
+    at zero after each call."""
+    monkeypatch.setenv("W12_MAX_GRID", str(grid))
+    w, _ = case(name)
+    n, k = w.shape
+    plan = w12.gemm_plan(m, n, k)
+    assert plan["grid"] <= grid
+    t = w12.encode(dev_weights(w))
+    x = S.activations(m, k, 900 + m)
+    ld = (k + 7) // 8 * 8
+    xd = to_dev(x, ld)
+    ws = w12.gemm_workspace(m, n, k)
+    cb = plan["counter_bytes"]
+    outs = []
+    for _ in range(8):
+        ws[cb:].view(torch.uint8).fill_(0xFF)   # NaN partials: a read of an unwritten slot shows
+        outs.append(w12.gemm(xd, t, ws=ws).cpu().numpy().view(np.uint32))
+        assert (ws[:cb].cpu().numpy() == 0).all(), "arrival counters must return to zero"
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    bad, worst = O.gemm_check(x, w, outs[0].view(np.float32))
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
+
+
 def test_gemm_workspace_reused_across_shapes():
     """One workspace, sized for the largest call, serves calls of different shapes in turn."""
     w, _ = case("gauss_300x4096")
