@@ -159,7 +159,7 @@ int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
 /* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
   int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles                       */
-  int32_t splits;            /* K slices per output tile                                 */
+  int32_t splits;            /* most K slices (partial sums) of one output tile          */
   int32_t rows_per_block;    /* rows of W per work-group tile                            */
   int32_t m_tile;            /* rows of X per work-group tile                            */
   int64_t grid;              /* work-groups launched                                     */

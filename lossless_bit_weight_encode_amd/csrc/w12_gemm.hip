@@ -1011,9 +1011,19 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
     if (4 * p.tiles * s >= 3 * G) G = p.tiles * s;
   }
   p.grid = G;
-  // segments per tile (1 when every work-group covers whole tiles)
-  p.splits = (int)((p.upt * G + p.units - 1) / p.units);
-  if (p.splits < 1) p.splits = 1;
+  // most segments (work-group ranges) meeting one tile: 1 + the range starts strictly inside it
+  {
+    int64_t best = 1, run_tile = -1, run = 0;
+    for (int64_t w = 1; w < G; ++w) {
+      const int64_t u = w * p.units / G;
+      if (u % p.upt == 0) continue;
+      const int64_t t = u / p.upt;
+      run = (t == run_tile) ? run + 1 : 1;
+      run_tile = t;
+      best = run + 1 > best ? run + 1 : best;
+    }
+    p.splits = (int)best;
+  }
   const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
   p.counter_bytes = ((uint64_t)p.tiles * 4 + 255) / 256 * 256;
   p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
