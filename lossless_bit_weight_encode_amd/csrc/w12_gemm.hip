@@ -6,23 +6,24 @@
 //   * streams the hi/lo record planes from HBM into a per-wave two-stage LDS ring with
 //     buffer-to-LDS DMA loads (no registers held while a stage is in flight), reads each
 //     lane's 16 + 8 bytes back, decodes them to BF16 pairs in registers (decode16) and
-//     patches the escapes of the lane's own k range through a cursor over its channel's
-//     ascending escape list;
-//   * M <= 8: FP32 dot2 (v_dot2c_f32_bf16) accumulation per lane, a fixed butterfly over the
-//     4 lane groups and a fixed wave order through LDS (wavefront GEMV); X rides the ring;
-//   * M >= 9: the decoded chunk is the B operand of v_mfma_f32_16x16x32_bf16 (16 rows of W x
+//     patches the escapes of the lane's chunk from its channel's escape list, which sits in
+//     LDS (copied one segment ahead);
+//   * small M (the wavefront GEMV): FP32 dot2 (v_dot2c_f32_bf16) accumulation per lane, a
+//     fixed butterfly over the 4 lane groups and a fixed wave order through LDS; X rides the
+//     ring;
+//   * larger M: the decoded chunk is the B operand of v_mfma_f32_16x16x32_bf16 (16 rows of W x
 //     32 k) and X rows (padded to 16) are the A operand, double-buffered in registers;
-//   * schedules work stream-K style: the grid is the number of work-groups resident at once,
-//     and work-group w takes the contiguous range [w U / G, (w+1) U / G) of the U = tiles x
-//     units work units (a unit is 16 chunks of one tile), so every work-group streams the
+//   * schedules work stream-K style: the grid is at most the number of work-groups resident at
+//     once, and work-group w takes the contiguous range [w U / G, (w+1) U / G) of the U = tiles
+//     x units work units (a unit is 16 chunks of one tile), so every work-group streams the
 //     same number of bytes.  A tile covered by several work-groups gets one partial per
 //     segment; the last segment to finish sums them in segment order (a fixed order set by
 //     (M, N, K, G)), with no floating-point atomics.
 //
-// Inside a segment: a tile is RB row blocks (16 rows each) x one m tile.  The segment's chunk
-// range is cut into 16 contiguous sub-ranges, one per (wave w, lane group g) pair; lane
-// (r = lane % 16, g = lane / 16) of wave w handles row r of every row block of the tile on
-// sub-range 4w + g, so the X values it loads serve RB row blocks.
+// Inside a segment: a tile is RB row blocks (16 rows each) x one m tile.  Lane (r = lane % 16,
+// g = lane / 16) of wave w belongs to lane group q = 4 w + g and handles row r of every row
+// block of the tile on the chunks of lane group q, so the X values it loads serve RB row
+// blocks.
 #include <mutex>
 
 #include "w12_device.h"
