@@ -25,6 +25,7 @@
 // block of the tile on the chunks of lane group q, so the X values it loads serve RB row
 // blocks.
 #include <mutex>
+#include <type_traits>
 
 #include "w12_device.h"
 #include "w12_kernels.h"
@@ -285,14 +286,17 @@ struct GemvPath {
   struct XStage {
     uint4 x[kWaves][kWave];   // [m][g][half]
   };
+  // the lane group whose chunks this lane fetches X for (both X loads)
+  __device__ static void x_groups(int wave, int lane, int& q0, int& q1) { q0 = q1 = wave * 4 + ((lane >> 1) & 3); }
   // lanes l < 8M fetch (m = l / 8, lane group l / 2 % 4, half l % 2)
-  __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, uint32_t xc0, uint32_t xc_end,
-                                 uint32_t stride, uint32_t j, XStage* xs, int wave) {
+  __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, const uint32_t xc0[2],
+                                 const uint32_t xc_end[2], uint32_t stride, int /*m0*/, uint32_t j, XStage* xs,
+                                 int wave) {
     const int lane = threadIdx.x & 63;
     const uint32_t m = (uint32_t)lane >> 3, half = lane & 1;
-    const uint32_t c = xc0 + stride * j;
-    const uint32_t off = (m < (uint32_t)M && c < xc_end) ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
-                                                        : kOutOfRange;
+    const uint32_t c = xc0[0] + stride * j;
+    const uint32_t off = (m < (uint32_t)M && c < xc_end[0]) ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
+                                                           : kOutOfRange;
     dma16(rx, &xs->x[wave][0], off);
   }
   __device__ static void zero(Acc acc[]) {
@@ -303,6 +307,11 @@ struct GemvPath {
   __device__ static uint32_t x_addr(const XStage* xs, int wave) {
     const int gq = (threadIdx.x & 63) >> 4;
     return lds_off(&xs->x[wave][gq * 2]);
+  }
+  // one stage's W bytes and X pieces of this lane
+  __device__ static void read_stage(uint32_t ah, uint32_t al, const XStage* xs, int wave, uint4 h[4], uint2 l[4],
+                                    uint4 xa[M], uint4 xb[M]) {
+    read_stage_wx<M>(ah, al, x_addr(xs, wave), h, l, xa, xb);
   }
   __device__ static void mac(const uint32_t d[8], const uint4 xa[M], const uint4 xb[M], Acc acc[]) {
 #pragma unroll
@@ -345,17 +354,55 @@ struct GemvPath {
   }
 };
 
-// M >= 9: MB m blocks of 16 rows; lane (r, g) supplies X row m0 + 16 mb + r of its own chunk,
-// loaded one iteration ahead into registers.
+// MFMA tiles: MB m blocks of 16 rows; lane (r, g) supplies X row m0 + 16 mb + r of its own
+// chunk.  One block (up to 16 rows): X rides the LDS ring like W, so no register load is in
+// flight across a step and the compiler adds no waits of its own to the loop.  More blocks:
+// X is loaded one step ahead into registers (the LDS would not hold two work-groups per CU).
 template <int MB>
 struct MfmaPath {
   static constexpr int kMRows = MB * 16;
   static constexpr int kWavesPerEU = MB <= 2 ? 2 : 1;   // register budget: two work-groups per CU up to 32 rows
-  static constexpr bool kXInLds = false;
-  static constexpr int kVmemPerStage = 6 + 2 * MB;   // 6 W DMA + X loads
+  static constexpr bool kXInLds = MB == 1;
+  static constexpr int kVmemPerStage = 6 + 2 * MB;   // 6 W DMA + 2 MB X loads
   typedef f32x4 Acc;
   static constexpr int kAcc = MB;
-  struct XStage {};
+  struct XLds {
+    uint4 x[kWaves][2 * kWave];   // per wave [lane group][row][half]: 32 bytes per (lane group, row)
+  };
+  struct XNone {};
+  typedef typename std::conditional<kXInLds, XLds, XNone>::type XStage;
+  // the lane groups whose chunks this lane fetches X for: load d covers lane groups 2d, 2d + 1
+  __device__ static void x_groups(int wave, int lane, int& q0, int& q1) {
+    q0 = wave * 4 + (lane >> 5);
+    q1 = q0 + 2;
+  }
+  // X load d, lane l: row m0 + (l / 2) % 16, half l % 2 of lane group 2d + l / 32; lane l of a
+  // load lands at 16 l, i.e. at (lane group, row, half) = ((l / 32 + 2d) * 16 + row) * 32 + 16 half
+  __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, const uint32_t xc0[2],
+                                 const uint32_t xc_end[2], uint32_t stride, int m0, uint32_t j, XStage* xs,
+                                 int wave) {
+    if constexpr (kXInLds) {
+      const int lane = threadIdx.x & 63;
+      const uint32_t m = (uint32_t)(m0 + ((lane >> 1) & 15)), half = lane & 1;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t c = xc0[d] + stride * j;
+        const uint32_t off = (m < (uint32_t)g.M && c < xc_end[d])
+                                 ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
+                                 : kOutOfRange;
+        dma16(rx, &xs->x[wave][d * kWave], off);
+      }
+    }
+  }
+  __device__ static uint32_t x_addr(const XStage* xs, int wave) {
+    const int lane = threadIdx.x & 63;
+    return lds_off(&xs->x[wave][0]) + (uint32_t)(((lane >> 4) * 16 + (lane & 15)) * 32);
+  }
+  __device__ static void read_stage(uint32_t ah, uint32_t al, const XStage* xs, int wave, uint4 h[4], uint2 l[4],
+                                    uint4 xa[MB], uint4 xb[MB]) {
+    if constexpr (kXInLds) read_stage_wx<1>(ah, al, x_addr(xs, wave), h, l, xa, xb);
+    else read_stage_w(ah, al, h, l);
+  }
   __device__ static void load_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, int m0, uint32_t c, bool ok, uint4 xa[MB],
                                 uint4 xb[MB]) {
     const int r = threadIdx.x & 15;
@@ -490,6 +537,20 @@ __device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t re, uint32_t 
                                            (int)((s0 + (uint32_t)(wave * kWave * 4 + lane * 4)) * 4u), 0, 0, 0);
 }
 
+// A global-memory escape entry, waited for on the spot.  The compiler cannot tell the two
+// escape modes apart at a cursor's later uses; a cursor register left with a load in flight
+// would make it wait for all vector-memory traffic (the ring's stages included) at every step.
+__device__ __forceinline__ uint32_t esc_global(const uint32_t* __restrict__ esc, uint32_t i) {
+  uint32_t v;
+  const uint32_t* p = esc + i;
+  asm volatile("global_load_dword %0, %1, off\n"
+               "s_waitcnt vmcnt(0)"
+               : "=v"(v)
+               : "v"(p)
+               : "memory");
+  return v;
+}
+
 struct LaneEsc {
   uint32_t pos, end;   // next entry and end of the channel's list (slice-relative in LDS mode)
   uint32_t e;          // the entry at pos (valid when pos < end)
@@ -513,7 +574,7 @@ __device__ __forceinline__ void esc_start(LaneEsc& c, const GemmArgs& g, uint32_
   } else {
     c.pos = lower_bound_k(g.esc, lo, hi, k_lo);
     c.end = hi;
-    c.e = c.pos < c.end ? g.esc[c.pos] : 0u;
+    c.e = c.pos < c.end ? esc_global(g.esc, c.pos) : 0u;
   }
 }
 
@@ -524,7 +585,7 @@ __device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict
   while (c.pos < c.end && (c.e >> 16) < k0 + kChunkK) {
     if ((c.e >> 16) >= k0) patch16(d, (c.e >> 16) - k0, c.e & 0xFFFFu);
     ++c.pos;
-    if (c.pos < c.end) c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc[c.pos];
+    if (c.pos < c.end) c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc_global(esc, c.pos);
   }
 }
 
@@ -534,9 +595,10 @@ struct SegGeo {
   int m0;
   SegLane sl;
   uint32_t soff_h[kRB];
-  uint32_t xc0, xc_end;    // chunks of the lane group this lane fetches X for (GEMV: 4 wave + lane / 2 % 4)
+  uint32_t xc0[2], xc_end[2];   // chunks of the lane groups this lane fetches X for (Path::x_groups)
 };
 
+template <class Path>
 __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t u_end, bool interleaved, SegGeo& s) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int q = wave * 4 + (lane >> 4);
@@ -551,21 +613,28 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t 
   const int64_t cs1 = ((s.seg_end - s.t0) * kUnitChunks < g.Kc) ? (s.seg_end - s.t0) * kUnitChunks : g.Kc;
   SegLane& sl = s.sl;
   const int qd = wave * 4 + ((lane >> 3) & 3);
-  const int qx = wave * 4 + ((lane >> 1) & 3);
+  int qx[2];
+  Path::x_groups(wave, lane, qx[0], qx[1]);
   sl.c_end = (uint32_t)cs1;
   sl.iters = (uint32_t)ceil_div(cs1 - cs0, kSubRanges);
   if (interleaved) {
     sl.stride = kSubRanges;
     sl.c0 = (uint32_t)(cs0 + q);
     sl.cd0 = (uint32_t)(cs0 + qd);
-    s.xc0 = (uint32_t)(cs0 + qx);
-    s.xc_end = (uint32_t)cs1;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      s.xc0[d] = (uint32_t)(cs0 + qx[d]);
+      s.xc_end[d] = (uint32_t)cs1;
+    }
   } else {
     sl.stride = 1;
     sl.c0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q));
     sl.cd0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qd));
-    s.xc0 = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx));
-    s.xc_end = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx + 1));
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      s.xc0[d] = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx[d]));
+      s.xc_end[d] = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, qx[d] + 1));
+    }
     // a contiguous share ends where the next lane group's begins
     sl.c_end = (uint32_t)(cs0 + split_point(cs1 - cs0, kSubRanges, q + 1));
   }
@@ -640,11 +709,11 @@ void k_gemm(GemmArgs g) {
   // ---- prologue: stage 0 of the first segment (interleaved mapping assumed) alongside its
   // escape metadata, then the escape slice ----
   SegGeo cur;
-  seg_setup(g, u_first, u_end, true, cur);
+  seg_setup<Path>(g, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
   auto issue_stage0 = [&]() {
     issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
-    if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, 0, &xring0, wave);
+    if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, 0, &xring0, wave);
     else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
   };
   issue_stage0();
@@ -655,7 +724,7 @@ void k_gemm(GemmArgs g) {
   if ((s1 - s0) > (uint32_t)kSliceEntries) {
     // escape lists too long for LDS: contiguous mapping; stage 0 again (the first copy has landed)
     wait_vmcnt<0>();
-    seg_setup(g, u_first, u_end, false, cur);
+    seg_setup<Path>(g, u_first, u_end, false, cur);
     issue_stage0();
   }
   issue_slice(re, s0, &slices[0][0], wave);
@@ -766,8 +835,7 @@ void k_gemm(GemmArgs g) {
       static_assert(RB == 4, "ring reads are written for 4 row blocks");
       uint4 h[RB];
       uint2 l[RB];
-      if constexpr (Path::kXInLds) read_stage_wx<Path::kAcc>(ah, al, Path::x_addr(xs, wave), h, l, xa, xb);
-      else read_stage_w(ah, al, h, l);
+      Path::read_stage(ah, al, xs, wave, h, l, xa, xb);
       const uint32_t c = cur.sl.c0 + cur.sl.stride * j;
       const bool valid = c < cur.sl.c_end;
       const uint32_t k0 = c * kChunkK;
@@ -785,7 +853,7 @@ void k_gemm(GemmArgs g) {
       int pend = 0;
       if (more1) {
         issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 1, &xring1, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, j + 1, &xring1, wave);
         else {
           const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
           Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa1, xb1);
@@ -803,7 +871,7 @@ void k_gemm(GemmArgs g) {
       pend = 0;
       if (more2) {
         issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
-        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, j + 2, &xring0, wave);
+        if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, j + 2, &xring0, wave);
         else {
           const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
           Path::load_x(g, rx, cur.m0 * MROWS, cx, cx < cur.sl.c_end, xa0, xb0);
@@ -862,14 +930,14 @@ void k_gemm(GemmArgs g) {
     if (!has_next) break;
     {
       SegGeo nx;
-      seg_setup(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+      seg_setup<Path>(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
       issue_w<RB>(g, rh, rl, nx.soff_h, nx.sl, 0, &ring0, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, 0, &xring0, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
       else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
     }
     barrier();   // red is free again; the next slice is visible to every wave
     // switch to the next segment
-    seg_setup(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
+    seg_setup<Path>(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
     sb ^= 1;
     in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
 #pragma unroll
