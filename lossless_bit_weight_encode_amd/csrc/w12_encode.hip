@@ -12,33 +12,56 @@
 namespace w12 {
 
 constexpr int kCountWaves = 4;
+constexpr int kCountBatch = 8;   // 16-byte loads per lane in flight before they are counted
+constexpr int kHistCopies = 8;   // histogram copies per wave (lane % 8 picks one)
+constexpr int kHistStride = 257; // words per copy: copies of one bin fall in different banks
 
-// One wave per channel: LDS exponent histogram, then the best 16-wide window.
+// One wave per channel: LDS exponent histogram, then the best 16-wide window.  Each lane
+// issues kCountBatch loads (8 KB per wave) before counting them, so a wave is not limited to
+// one memory round trip per KB of its row.  A channel's exponents sit in a handful of bins,
+// so the 64 lanes' atomic adds would mostly hit the same few words; eight copies of the
+// histogram (summed at the end) cut those collisions eightfold.
 __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
     const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, const uint8_t* __restrict__ forced,
     uint8_t* __restrict__ base, uint32_t* __restrict__ esc_ptr) {
-  __shared__ uint32_t hist[kCountWaves][256];
+  __shared__ uint32_t hist[kCountWaves][kHistCopies * kHistStride];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * kCountWaves + wave;
-  uint32_t* h = hist[wave];
-  for (int i = lane; i < 256; i += kWave) h[i] = 0;
+  uint32_t* const hw = hist[wave];
+  uint32_t* const h = hw + (lane % kHistCopies) * kHistStride;   // this lane's copy
+  for (int i = lane; i < kHistCopies * kHistStride; i += kWave) hw[i] = 0;
   __syncthreads();
   if (n < N) {
     const uint16_t* row = W + n * ldw;
-    for (int k = lane * 8; k < K; k += kWave * 8) {
-      uint32_t v[4];
-      if (k + 8 <= K) {
-        const uint4 q = *reinterpret_cast<const uint4*>(row + k);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    const int full = K / 8;   // whole 8-element groups
+    for (int g0 = 0; g0 < full; g0 += kCountBatch * kWave) {
+      uint4 q[kCountBatch];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          atomicAdd(&h[(v[i] >> 7) & 0xFFu], 1u);
-          atomicAdd(&h[(v[i] >> 23) & 0xFFu], 1u);
+      for (int i = 0; i < kCountBatch; ++i) {
+        const int gi = g0 + i * kWave + lane;
+        q[i] = gi < full ? *reinterpret_cast<const uint4*>(row + 8 * gi) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kCountBatch; ++i) {
+        if (g0 + i * kWave + lane < full) {
+          const uint32_t v[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            atomicAdd(&h[(v[j] >> 7) & 0xFFu], 1u);
+            atomicAdd(&h[(v[j] >> 23) & 0xFFu], 1u);
+          }
         }
-      } else {
-        for (int i = k; i < K; ++i) atomicAdd(&h[(row[i] >> 7) & 0xFFu], 1u);
       }
     }
+    for (int i = 8 * full + lane; i < K; i += kWave) atomicAdd(&h[(row[i] >> 7) & 0xFFu], 1u);
+  }
+  __syncthreads();
+  // fold the copies into copy 0
+  for (int e = lane; e < 256; e += kWave) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kHistCopies; ++i) c += hw[i * kHistStride + e];
+    hw[e] = c;
   }
   __syncthreads();
   if (n < N) {
@@ -47,7 +70,7 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
       uint32_t b = forced[n];
       b = b < 1u ? 1u : (b > 239u ? 239u : b);
       uint32_t c = 0;
-      for (uint32_t e = b; e < b + 16; ++e) c += h[e];
+      for (uint32_t e = b; e < b + 16; ++e) c += hw[e];
       best = (c << 8) | (255u - b);
     } else {
       // key = count << 8 | (255 - b): the max key has the largest count and, among equal
@@ -56,7 +79,7 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
       for (int b = lane + 1; b <= 239; b += kWave) {
         uint32_t c = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) c += h[b + e];
+        for (int e = 0; e < 16; ++e) c += hw[b + e];
         const uint32_t key = (c << 8) | (255u - (uint32_t)b);
         best = key > best ? key : best;
       }
