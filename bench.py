@@ -82,7 +82,17 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE run, WRITE_SIZE run of "
                          "--only-layer --copy-probe) into the per-launch traffic summary under profiles/")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only the batched-verify GEMMs (gate_up and down at M=256 and 512, three launches "
+                         "each on rotating copies), for MFMA counters; prints their event times as JSON")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("PMC_CSV", "PROBE_JSON"),
+                    help="turn a rocprofv3 --pmc run of --mfma-probe (SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and the probe's own output into the "
+                         "MFMA summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
         return
@@ -98,6 +108,9 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     m_step = 16
+    if args.mfma_probe:
+        mfma_probe(dev, stream)
+        return
 
     # ---- inputs (synthetic, seeded; host-generated so bits do not depend on the GPU) ----
     t0 = time.time()
@@ -249,6 +262,93 @@ def main():
     # ---- CPU oracle on the host cores (a reported baseline, not the target) ----
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer, enc)
+    print(json.dumps(out))
+
+
+MFMA_PROBE_M = (256, 512)
+MFMA_PROBE_MATS = ("gate_up", "down")
+
+
+def mfma_probe(dev, stream):
+    """gate_up and down at M = 256 and 512 (the batched-verify tiles), three launches each on
+    three rotating encoded copies, in a fixed order; prints the per-launch event times."""
+    layer = S.layer(0, which=MFMA_PROBE_MATS)
+    res = {}
+    for nm in MFMA_PROBE_MATS:
+        n, k = S.LAYER_SHAPES[nm]
+        e0 = w12.encode(dev_bits(layer[nm]))
+        cs = [e0, clone_tensor(e0), clone_tensor(e0)]
+        for m in MFMA_PROBE_M:
+            x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
+            y = torch.empty(m, n, dtype=torch.float32, device=dev)
+            ws = w12.gemm_workspace(m, n, k)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                w12.gemm(x, cs[i], y=y, ws=ws, stream=stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            plan = w12.gemm_plan(m, n, k)
+            res[f"{nm}_M{m}"] = {"kernel": kernel_name(plan, m), "launch_us": [round(a.elapsed_time(b) * 1e3, 2)
+                                                                              for a, b in evs],
+                                 "flops": 2 * m * n * k, "grid": plan["grid"], "m_tile": plan["m_tile"]}
+        del cs, e0
+        torch.cuda.empty_cache()
+    print(json.dumps(res))
+
+
+def summarize_mfma(pmc_csv, probe_json):
+    """MFMA busy fraction and BF16 MFMA FLOP rate of the --mfma-probe GEMM launches.  Per
+    dispatch: util = SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GPU-active cycles x SIMDs),
+    where the GPU-active cycles are GRBM_GUI_ACTIVE / XCDs (the CSV sums the counter over the
+    XCDs); MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; the rate uses the probe's own event
+    time of the launch (the middle one of each three, in the fixed launch order).  SIMD and XCD
+    counts come from the run's agent info."""
+    rows = _counter_rows(pmc_csv)
+    by_disp = {}
+    for r in rows:
+        if "k_gemm" not in r["Kernel_Name"]:
+            continue
+        d = by_disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[i] for i in sorted(by_disp)]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    import csv
+    agent_csv = os.path.join(os.path.dirname(pmc_csv), os.path.basename(pmc_csv).replace("counter_collection",
+                                                                                         "agent_info"))
+    simds, xcds = 1024, 8
+    if os.path.exists(agent_csv):
+        with open(agent_csv) as f:
+            for r in csv.DictReader(f):
+                if r.get("Name", "").startswith("gfx"):
+                    simds, xcds = int(r["Simd_Count"]), int(r["Num_Xcc"])
+    out = {"commands": [
+        "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE -f csv "
+        "-d gpurun_out/pmc_mfma -o run -- python3 bench.py --mfma-probe",
+        "python3 bench.py --mfma-probe > gpurun_out/mfma_probe.json",
+        f"python3 bench.py --summarize-mfma {pmc_csv} {probe_json}"],
+        "simds": simds, "xcds": xcds, "peak_bf16_dense_TFLOPs": 2500.0, "launches": {}}
+    i = 0
+    for nm in MFMA_PROBE_MATS:
+        for m in MFMA_PROBE_M:
+            key = f"{nm}_M{m}"
+            ds = disp[i:i + 3]
+            i += 3
+            mid = ds[1]
+            t_us = probe[key]["launch_us"][1]
+            util = mid["SQ_VALU_MFMA_BUSY_CYCLES"] / (mid["GRBM_GUI_ACTIVE"] / xcds * simds)
+            mflops = mid["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            out["launches"][key] = {
+                "kernel": probe[key]["kernel"], "grid": probe[key]["grid"], "m_tile": probe[key]["m_tile"],
+                "launch_us": t_us, "mfma_busy_frac": round(util, 4),
+                "mfma_flops": mflops, "useful_flops": probe[key]["flops"],
+                "mfma_TFLOPs": round(mflops / t_us / 1e6, 1),
+                "useful_TFLOPs": round(probe[key]["flops"] / t_us / 1e6, 1),
+                "frac_of_bf16_peak": round(probe[key]["flops"] / t_us / 1e6 / 2500.0, 4)}
+    path = os.path.join(ROOT, "profiles", "gemm_M256_M512_mfma_counters.txt")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
