@@ -706,8 +706,8 @@ void k_gemm(GemmArgs g) {
   const uint32_t slice_addr0 = lds_off(&slices[0][0]), slice_addr1 = lds_off(&slices[1][0]);
   const uint32_t red_addr = lds_off(&red[0]);
 
-  // ---- prologue: stage 0 of the first segment (interleaved mapping assumed) alongside its
-  // escape metadata, then the escape slice ----
+  // ---- prologue: the first segment's escape metadata and stage 0 (interleaved mapping
+  // assumed), then the escape slice ----
   SegGeo cur;
   seg_setup<Path>(g, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
@@ -716,11 +716,12 @@ void k_gemm(GemmArgs g) {
     if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, 0, &xring0, wave);
     else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
   };
-  issue_stage0();
+  // the escape pointers first: the slice that depends on them completes behind stage 0 anyway
   SegEsc se;
   load_seg_esc(g, rp, rbase, cur.rg, se);
+  issue_stage0();
   uint32_t s0, s1;
-  slice_range(g, cur.rg, se, s0, s1);   // waits for the loads above (and so for stage 0)
+  slice_range(g, cur.rg, se, s0, s1);   // waits for the escape loads only (stage 0 is newer)
   if ((s1 - s0) > (uint32_t)kSliceEntries) {
     // escape lists too long for LDS: contiguous mapping; stage 0 again (the first copy has landed)
     wait_vmcnt<0>();
