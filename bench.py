@@ -44,6 +44,16 @@ def alg_bytes(n, k, m, e):
     return 1.5 * n * k + n + 4 * (n + 1) + 4 * e + 2 * m * k + 4 * m * n
 
 
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def byte_floor_us(n, k, m, e):
+    """The pages' floor for a kernel: the larger of its FLOP time at 60% of the dense BF16 peak
+    and its byte time at 90% of the HBM peak (SpecPilot summary page, the ceiling bullet
+    attributed to section 3.1)."""
+    return max(2.0 * m * n * k / (0.6 * BF16_PEAK_TFLOPS * 1e6), alg_bytes(n, k, m, e) / (0.9 * HBM_PEAK_GBPS * 1e3))
+
+
 def dev_bits(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
 
@@ -200,7 +210,10 @@ def main():
             "bytes_moved_per_step": int(moved),
             "bytes_moved_GBps": round(moved / t_step / 1e6, 1),
             "bytes_moved_frac_of_8TBps": round(moved / t_step / 1e6 / HBM_PEAK_GBPS, 4),
+            "byte_floor_us": round(sum(byte_floor_us(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes)
+                                       for nm in names), 2),
             "rotated_copies": len(copies),
+            "inputs_sha256": {nm: S.sha256(layer[nm])[:16] for nm in names},
         },
     }
     if args.only_layer:
@@ -243,9 +256,11 @@ def main():
                     w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm)
                 t = timed(lambda i: w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm), 30, stream)
                 ab = alg_bytes(n, k, m, enc[nm].num_escapes)
+                fl = byte_floor_us(n, k, m, enc[nm].num_escapes)
                 sweep[f"{nm}_M{m}"] = {
                     "us": round(t * 1e3, 2), "weight_GBps": round(2 * n * k / t / 1e6, 1),
                     "moved_GBps": round(ab / t / 1e6, 1), "frac": round(ab / t / 1e6 / HBM_PEAK_GBPS, 4),
+                    "byte_floor_us": round(fl, 2), "floor_over_time": round(fl / (t * 1e3), 4),
                     "splits": w12.gemm_plan(m, n, k)["splits"],
                 }
                 log(f"[bench] {nm} M={m}: {t * 1e3:.1f} us, {ab / t / 1e6:.0f} GB/s moved")
