@@ -20,6 +20,9 @@ Sources (SpecPilot, arXiv 2611.02501, as summarised on its web pages):
   output channel; each weight becomes 12 bits (sign, 4-bit exponent offset, 7-bit
   mantissa); weights whose exponent lies outside the preset range go to a sparse
   list and are restored exactly; the original weights are recovered bit for bit.
+* [Article-TLV]  news article, part "(3) two-level verification": the first pass
+  verifies at low precision with the 8-bit weight view nested in W12, yields a
+  candidate chain but accepts nothing; only the later exact pass accepts tokens.
 
 Readings where the pages are silent (each is also listed in the design notes):
 
@@ -40,6 +43,12 @@ Readings where the pages are silent (each is also listed in the design notes):
       exact BF16 x BF16 products, and an output y passes when
       |y - y_ref| <= 2^-12 * sum_k |x_k * w_k|; where y_ref is +-inf, y must be the
       same infinity; where y_ref is NaN, y must be NaN.
+* R14 the nested 8-bit view of a record is its top byte, sign | offset | top three
+      mantissa bits; read as a weight it is the BF16 value with the four low mantissa
+      bits cleared (truncation toward zero);
+* R15 in the Q pass escaped weights keep their exact value (the escape list is the
+      format's only copy of them); the Q-pass GEMM is the R8 GEMM on the Q-view
+      weights, with the same tolerance.
 """
 from __future__ import annotations
 
@@ -178,6 +187,24 @@ def verify(t: W12Logical, ref: np.ndarray) -> tuple[int, int]:
     return int(bad.size), (int(bad[0]) if bad.size else -1)
 
 
+def q_view(t: W12Logical) -> np.ndarray:
+    """R14/R15: the weights the Q pass reads, as BF16 bits.  In-window positions take the
+    record's top byte (sign, offset, three mantissa bits) re-biased by the channel base, with
+    the four low mantissa bits zero; escaped positions take their exact escape value."""
+    top = (t.rec.astype(np.uint32) >> 4) & 0xFF
+    s = top >> 7
+    off = (top >> 3) & 0xF
+    m3 = top & 0x7
+    e = off + t.base.astype(np.uint32)[:, None]
+    out = ((s << 15) | (e << 7) | (m3 << 4)).astype(np.uint16)
+    for row in range(t.n):
+        lo, hi = int(t.esc_ptr[row]), int(t.esc_ptr[row + 1])
+        if hi > lo:
+            ent = t.esc[lo:hi]
+            out[row, (ent >> 16).astype(np.int64)] = (ent & 0xFFFF).astype(np.uint16)
+    return out
+
+
 def bits_per_weight(n: int, k: int, e: int) -> float:
     """R7: stored bits per weight of the logical format."""
     return (1.5 * n * k + n + 4 * (n + 1) + 4 * e) * 8.0 / (n * k)
@@ -235,3 +262,12 @@ def gemm_check(x: np.ndarray, w: np.ndarray, y: np.ndarray) -> tuple[int, float]
     fin = np.isfinite(y_ref) & (a_ref > 0)
     worst = float(np.max(np.abs(np.asarray(y, np.float64)[fin] - y_ref[fin]) / a_ref[fin])) if fin.any() else 0.0
     return int((~ok).sum()), worst
+
+
+def gemm_q_check(x: np.ndarray, t: W12Logical, y: np.ndarray, rows=None) -> tuple[int, float]:
+    """R15: the Q-pass GEMM checked as the R8 GEMM on the Q-view weights (optionally on a
+    subset of output channels: y then holds only those columns)."""
+    wq = q_view(t)
+    if rows is not None:
+        wq = wq[np.asarray(rows)]
+    return gemm_check(x, wq, y)
