@@ -156,6 +156,18 @@ int w12_gemm_workspace_init(void *ws, uint64_t ws_bytes, hipStream_t stream);
 int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
              float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
 
+/*
+ * The Q pass of two-level verification (news article, two-level verification part: the
+ * first pass verifies at low precision with the 8-bit weight view nested in W12 and accepts
+ * nothing).  Y = X . Wq^T, where Wq is W with every in-window weight read through the
+ * record's top byte (sign, exponent offset, three mantissa bits), i.e. truncated toward zero
+ * to four significant bits, and every escaped weight exact.  Only the hi plane of the records
+ * is read (1 byte per weight).  Same arguments, layouts, workspace, errors, tolerance (against
+ * the FP64 product with Wq) and run-to-run determinism as w12_gemm.
+ */
+int w12_gemm_q(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
+               float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
+
 /* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
   int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles                       */

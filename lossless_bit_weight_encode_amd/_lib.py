@@ -46,6 +46,7 @@ _SIGNATURES = {
     "w12_gemm_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_u64)]),
     "w12_gemm_workspace_init": (ctypes.c_int, [_c_p, _c_u64, _c_p]),
     "w12_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
+    "w12_gemm_q": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
     "w12_gemm_plan": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_PlanInfo)]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
     "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -256,8 +257,9 @@ def gemm_workspace(m: int, n: int, k: int, device="cuda", stream=None) -> torch.
 
 
 def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
-         stream=None) -> torch.Tensor:
-    """Y[M, N] (FP32) = X[M, K] (BF16) @ W^T with W12 weights.
+         stream=None, qpass: bool = False) -> torch.Tensor:
+    """Y[M, N] (FP32) = X[M, K] (BF16) @ W^T with W12 weights (qpass: the Q pass on the nested
+    8-bit view, w12_gemm_q).
 
     ws: a workspace from gemm_workspace() (or any buffer of at least gemm_workspace_size bytes
     initialised once with gemm_workspace_init); one is allocated here when omitted."""
@@ -270,7 +272,8 @@ def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch
         ws = gemm_workspace(m, t.n, t.k, x.device, stream)
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     d = t.descriptor()
-    _check("w12_gemm", lib().w12_gemm(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
+    name = "w12_gemm_q" if qpass else "w12_gemm"
+    _check(name, getattr(lib(), name)(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
                                       _stream(stream)))
     return y
 

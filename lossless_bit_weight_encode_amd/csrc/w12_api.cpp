@@ -158,8 +158,8 @@ int w12_gemm_workspace_init(void* ws, uint64_t ws_bytes, hipStream_t stream) {
   return hip_status(w12::init_gemm_workspace(ws, ws_bytes, stream), "gemm_workspace_init");
 }
 
-int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
-             uint64_t ws_bytes, hipStream_t stream) {
+static int gemm_call(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
+                     uint64_t ws_bytes, bool qpass, hipStream_t stream) {
   int rc = check_tensor(t);
   if (rc) return rc;
   if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
@@ -177,7 +177,17 @@ int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, flo
                 (unsigned long long)p.ws_bytes);
   if (p.ws_bytes && !ws) return fail(W12_ERR_INVALID_ARG, "ws is NULL");
   if (ws && !aligned(ws, 16)) return fail(W12_ERR_MISALIGNED, "ws must be 16-byte aligned");
-  return hip_status(w12::launch_gemm(p, X, M, ldx, t, Y, ldy, ws, stream), "gemm");
+  return hip_status(w12::launch_gemm(p, X, M, ldx, t, Y, ldy, ws, qpass, stream), qpass ? "gemm_q" : "gemm");
+}
+
+int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
+             uint64_t ws_bytes, hipStream_t stream) {
+  return gemm_call(X, M, ldx, t, Y, ldy, ws, ws_bytes, false, stream);
+}
+
+int w12_gemm_q(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
+               uint64_t ws_bytes, hipStream_t stream) {
+  return gemm_call(X, M, ldx, t, Y, ldy, ws, ws_bytes, true, stream);
 }
 
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {

@@ -243,8 +243,9 @@ struct SegLane {
   uint32_t lo_rb0, lo_rb1;             // lo plane offsets of the row blocks this lane copies
 };
 
-// Stage j of a segment into st.
-template <int RB>
+// Stage j of a segment into st.  The Q pass (kQ) reads only the hi plane: the nested 8-bit
+// view.
+template <int RB, bool kQ>
 __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
                                         const uint32_t soff_h[RB], const SegLane& sl, uint32_t j,
                                         RingStage<RB>* st, int wave) {
@@ -256,10 +257,12 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
-  const uint32_t cd = sl.cd0 + sl.stride * j;
-  const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
-  dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
-  if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
+  if constexpr (!kQ) {
+    const uint32_t cd = sl.cd0 + sl.stride * j;
+    const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
+    dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
+    if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
+  }
 }
 
 // Byte addresses (in LDS) of this lane's hi and lo slots of row block 0 of a stage.
@@ -670,13 +673,16 @@ __device__ __forceinline__ void wait_pending(int pend) {
 // ------------------------------------------------------------------------------------------
 // The kernel.
 // ------------------------------------------------------------------------------------------
-template <class Path>
+// kQ: the Q pass of two-level verification (news article, two-level verification part): the
+// same GEMM on the nested 8-bit view, i.e. every in-window weight with its four low mantissa
+// bits zero (the lo plane is never read: its ring slots hold zeros) and escapes exact.
+template <class Path, bool kQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
 void k_gemm(GemmArgs g) {
   constexpr int RB = kRB;
   constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
-  constexpr int V = Path::kVmemPerStage;
+  constexpr int V = Path::kVmemPerStage - (kQ ? 2 : 0);   // the Q pass issues no lo loads
   constexpr int TILE_ELEMS = ROWS * MROWS;
   constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;   // output elements per thread
   typedef typename Path::XStage XStage;
@@ -699,6 +705,16 @@ void k_gemm(GemmArgs g) {
   const int64_t u_first = ubeg(g, blockIdx.x);
   const int64_t u_end = ubeg(g, (int64_t)blockIdx.x + 1);
   if (u_first >= u_end) return;
+  if constexpr (kQ) {
+    // the lo slots of both ring stages read as zero nibbles (made visible by the prologue's
+    // barrier, before any stage is read)
+    uint4* lo0 = &ring0.lo[0][0];
+    uint4* lo1 = &ring1.lo[0][0];
+    for (int i = threadIdx.x; i < kWaves * RB * 32; i += kThreads) {
+      lo0[i] = make_uint4(0, 0, 0, 0);
+      lo1[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
 
   uint32_t ah0, al0, ah1, al1;
   ring_addr<RB>(&ring0, wave, ah0, al0);
@@ -712,7 +728,7 @@ void k_gemm(GemmArgs g) {
   seg_setup<Path>(g, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
   auto issue_stage0 = [&]() {
-    issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
+    issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
     if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, 0, &xring0, wave);
     else Path::load_x(g, rx, cur.m0 * MROWS, cur.sl.c0, cur.sl.c0 < cur.sl.c_end, xa0, xb0);
   };
@@ -853,7 +869,7 @@ void k_gemm(GemmArgs g) {
       const bool more1 = j + 1 < iters;
       int pend = 0;
       if (more1) {
-        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
+        issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, j + 1, &ring1, wave);
         if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, j + 1, &xring1, wave);
         else {
           const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 1);
@@ -871,7 +887,7 @@ void k_gemm(GemmArgs g) {
       const bool more2 = j + 2 < iters;
       pend = 0;
       if (more2) {
-        issue_w<RB>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
+        issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, j + 2, &ring0, wave);
         if constexpr (Path::kXInLds) Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, j + 2, &xring0, wave);
         else {
           const uint32_t cx = cur.sl.c0 + cur.sl.stride * (j + 2);
@@ -932,7 +948,7 @@ void k_gemm(GemmArgs g) {
     {
       SegGeo nx;
       seg_setup<Path>(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
-      issue_w<RB>(g, rh, rl, nx.soff_h, nx.sl, 0, &ring0, wave);
+      issue_w<RB, kQ>(g, rh, rl, nx.soff_h, nx.sl, 0, &ring0, wave);
       if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
       else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
     }
@@ -996,13 +1012,13 @@ static int device_cus() {
 // Resident work-groups per CU of one kernel variant, from the runtime occupancy calculator
 // (registers and LDS of the compiled kernel); when no device is visible, a conservative
 // estimate.  Cached per variant.
-template <class Path>
+template <class Path, bool kQ = false>
 static int occupancy_of(int fallback) {
   static std::once_flag once;
   static int v = 0;
   std::call_once(once, [fallback] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemm<Path>), kThreads, 0) ==
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemm<Path, kQ>), kThreads, 0) ==
             hipSuccess && n > 0)
       v = n;
     else {
@@ -1104,28 +1120,29 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
 }
 
 template <class Path>
-static void launch_path(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((k_gemm<Path>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+static void launch_path(const GemmPlan& p, const GemmArgs& a, bool qpass, hipStream_t stream) {
+  if (qpass) hipLaunchKernelGGL((k_gemm<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+  else hipLaunchKernelGGL((k_gemm<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
 }
 
-static void dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t stream) {
+static void dispatch(const GemmPlan& p, const GemmArgs& a, bool qpass, hipStream_t stream) {
   if (p.path == 1) {
     switch (a.M) {
-      case 1: launch_path<GemvPath<1>>(p, a, stream); break;
-      case 2: launch_path<GemvPath<2>>(p, a, stream); break;
-      case 3: launch_path<GemvPath<3>>(p, a, stream); break;
-      case 4: launch_path<GemvPath<4>>(p, a, stream); break;
-      case 5: launch_path<GemvPath<5>>(p, a, stream); break;
-      case 6: launch_path<GemvPath<6>>(p, a, stream); break;
-      case 7: launch_path<GemvPath<7>>(p, a, stream); break;
-      default: launch_path<GemvPath<8>>(p, a, stream); break;
+      case 1: launch_path<GemvPath<1>>(p, a, qpass, stream); break;
+      case 2: launch_path<GemvPath<2>>(p, a, qpass, stream); break;
+      case 3: launch_path<GemvPath<3>>(p, a, qpass, stream); break;
+      case 4: launch_path<GemvPath<4>>(p, a, qpass, stream); break;
+      case 5: launch_path<GemvPath<5>>(p, a, qpass, stream); break;
+      case 6: launch_path<GemvPath<6>>(p, a, qpass, stream); break;
+      case 7: launch_path<GemvPath<7>>(p, a, qpass, stream); break;
+      default: launch_path<GemvPath<8>>(p, a, qpass, stream); break;
     }
   } else {
     switch (p.m_tile / 16) {
-      case 1: launch_path<MfmaPath<1>>(p, a, stream); break;
-      case 2: launch_path<MfmaPath<2>>(p, a, stream); break;
-      case 3: launch_path<MfmaPath<3>>(p, a, stream); break;
-      default: launch_path<MfmaPath<4>>(p, a, stream); break;
+      case 1: launch_path<MfmaPath<1>>(p, a, qpass, stream); break;
+      case 2: launch_path<MfmaPath<2>>(p, a, qpass, stream); break;
+      case 3: launch_path<MfmaPath<3>>(p, a, qpass, stream); break;
+      default: launch_path<MfmaPath<4>>(p, a, qpass, stream); break;
     }
   }
 }
@@ -1139,7 +1156,7 @@ hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream) {
 }
 
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
-                       int64_t ldy, void* ws, hipStream_t stream) {
+                       int64_t ldy, void* ws, bool qpass, hipStream_t stream) {
   GemmArgs a;
   a.Kc = num_chunks(t->K);
   if (p.xpad_bytes) {
@@ -1179,7 +1196,7 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   a.counters = reinterpret_cast<uint32_t*>(ws);
   a.P = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes);
   a.p_bytes = (uint32_t)p.partial_bytes;
-  dispatch(p, a, stream);
+  dispatch(p, a, qpass, stream);
   return hipGetLastError();
 }
 

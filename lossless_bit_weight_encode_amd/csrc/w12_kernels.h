@@ -38,7 +38,8 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K);
 hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream);
+// qpass: the Q pass on the nested 8-bit view (hi plane only, escapes exact)
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
-                       int64_t ldy, void* ws, hipStream_t stream);
+                       int64_t ldy, void* ws, bool qpass, hipStream_t stream);
 
 }  // namespace w12

@@ -177,3 +177,33 @@ def test_config5_heavy_tail(name):
     check_verify(t, w)
     for m in (16, 256):
         check_gemm_sampled(t, w, m, S.x_seed(m, k), sample_rows(n, count=64, seed=m))
+
+
+# ---- the Q pass (nested 8-bit view) on the dense layer, M = 16, and the heavy tail ---------------
+@pytest.mark.parametrize("name", S.LAYER_ORDER)
+def test_config2_layer_qpass(name):
+    w = layer(0)[name]
+    n, k = w.shape
+    t = encoded(("layer0", name), w)
+    rows = sample_rows(n, count=96, seed=3)
+    x = S.activations(16, k, S.x_seed(16, k))
+    ws = w12.gemm_workspace(16, n, k)
+    y = w12.gemm(to_dev(x), t, ws=ws, qpass=True)
+    y2 = w12.gemm(to_dev(x), t, ws=ws, qpass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "Q-pass GEMM is not bitwise repeatable"
+    ref = O.encode(w[rows])
+    bad, worst = O.gemm_q_check(x, ref, y.cpu().numpy()[:, rows])
+    assert bad == 0, f"{bad} sampled Q-pass outputs outside tolerance (worst rel {worst:.3g})"
+
+
+def test_config5_heavy_tail_qpass():
+    w = heavy("down")
+    n, k = w.shape
+    t = encoded(("heavy", "down"), w)
+    rows = sample_rows(n, count=48, seed=9)
+    x = S.activations(16, k, S.x_seed(16, k))
+    y = w12.gemm(to_dev(x), t, ws=w12.gemm_workspace(16, n, k), qpass=True)
+    torch.cuda.synchronize()
+    bad, worst = O.gemm_q_check(x, O.encode(w[rows]), y.cpu().numpy()[:, rows])
+    assert bad == 0, f"{bad} sampled Q-pass outputs outside tolerance (worst rel {worst:.3g})"

@@ -184,6 +184,51 @@ def test_gemm_other_path_within_tolerance(monkeypatch, name, limit, ms):
         run_gemm_check(name, m, seed=1000)
 
 
+# ---------------------------------------------------------------------------------------
+# GEMM, Q pass (nested 8-bit view: hi plane only, escapes exact)
+# ---------------------------------------------------------------------------------------
+
+QPASS_M = [1, 2, 3, 16, 24, 33, 64, 100]
+
+
+@pytest.mark.parametrize("name", GEMM_SHAPES)
+@pytest.mark.parametrize("m", QPASS_M)
+def test_gemm_qpass_within_tolerance(name, m):
+    if name == "uniform_bits_100x520":
+        pytest.skip("random bit patterns overflow FP32 products; covered by encode/decode tests")
+    w, _ = case(name)
+    n, k = w.shape
+    x = S.activations(m, k, 700 + m)
+    ld = (k + 7) // 8 * 8
+    t = w12.encode(dev_weights(w))
+    y = w12.gemm(to_dev(x, ld), t, qpass=True)
+    torch.cuda.synchronize()
+    bad, worst = O.gemm_q_check(x, O.encode(w), y.cpu().numpy())
+    assert bad == 0, f"{bad} outputs outside tolerance of the Q-view product (worst rel {worst:.3g})"
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_gemm_qpass_bitwise_deterministic_and_differs_from_exact(m):
+    """Q pass: bitwise repeatable, counters back at zero, and a different product from the
+    exact pass (the weights have low mantissa bits set)."""
+    w, _ = case("gauss_300x4096")
+    n, k = w.shape
+    t = w12.encode(dev_weights(w))
+    x = to_dev(S.activations(m, k, 88 + m))
+    plan = w12.gemm_plan(m, n, k)
+    ws = w12.gemm_workspace(m, n, k)
+    cb = plan["counter_bytes"]
+    outs = []
+    for _ in range(10):
+        ws[cb:].view(torch.float32).fill_(float("nan"))
+        outs.append(w12.gemm(x, t, ws=ws, qpass=True).cpu().numpy().view(np.uint32))
+        assert (ws[:cb].cpu().numpy() == 0).all()
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    exact = w12.gemm(x, t, ws=ws).cpu().numpy().view(np.uint32)
+    assert not np.array_equal(exact, outs[0])
+
+
 @pytest.mark.parametrize("m", [1, 4, 8, 16, 32, 64, 100])
 def test_gemm_bitwise_deterministic(m):
     """20 runs bitwise identical; the partial region of the workspace is NaN-poisoned before
