@@ -243,6 +243,26 @@ def main():
     out["roofline"].update(traffic_from_profile(ab))
     out["load_time"] = load_leg
 
+    # ---- the Q pass (nested 8-bit view, hi plane only) of the same layer step ----
+    def q_step(i):
+        c = copies[i % len(copies)]
+        for nm in names:
+            w12.gemm(x_dev[(nm, m_step)], c[nm], y=y_dev[nm], ws=ws[nm], stream=stream, qpass=True)
+
+    for i in range(args.warmup):
+        q_step(i)
+    torch.cuda.synchronize()
+    t_q = timed(q_step, args.steps, stream)
+    moved_q = sum(alg_bytes(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes) - 0.5 * S.LAYER_SHAPES[nm][0] *
+                  S.LAYER_SHAPES[nm][1] for nm in names)
+    out["qpass"] = {
+        "what": "the same layer step through w12_gemm_q (hi plane only: 1 B/weight, escapes exact)",
+        "ms_per_step": round(t_q, 5), "weight_GBps": round(weight_bytes / t_q / 1e6, 1),
+        "bytes_moved_GBps": round(moved_q / t_q / 1e6, 1),
+        "bytes_moved_frac_of_8TBps": round(moved_q / t_q / 1e6 / HBM_PEAK_GBPS, 4),
+    }
+    log(f"[bench] Q-pass layer step {t_q * 1e3:.1f} us -> {weight_bytes / t_q / 1e6:.1f} weight-GB/s")
+
     # ---- tree-verify M sweep on gate_up and down ----
     if not args.no_sweep:
         sweep = {}
