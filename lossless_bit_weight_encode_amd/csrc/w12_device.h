@@ -48,41 +48,49 @@ __device__ __forceinline__ uint32_t add16x2(uint32_t x, uint32_t y) {
   return __builtin_bit_cast(uint32_t, a + b);
 }
 
-// Decode the 16 weights of one row of one chunk into 8 BF16 pairs (natural k order:
-// d[p] = w[2p] | w[2p+1] << 16).  bb2 = (b << 7) | (b << 23) for the channel's base b.
+// Decode 8 weights of one row of one chunk (k = 8 h .. 8 h + 7 for half h) into 4 BF16 pairs
+// (natural k order: d[p] = w[2p] | w[2p+1] << 16).  hw: the half's 8 hi bytes; l: its lo word
+// (lo bytes 4 h .. 4 h + 3 of the row).  bb2 = (b << 7) | (b << 23) for the channel's base b.
 //
 // Pair p: v_perm gathers hi bytes 2p, 2p+1 into the high byte of each 16-bit half and the
 // lo bytes holding their nibbles into the low byte (nibble in bits 7..4).  An arithmetic
 // shift by 4 then leaves sign in bit 15 (copied into bits 14..11), offset|mantissa in
 // bits 10..0; clearing bits 14..11 and adding b << 7 gives (off + b) << 7 in the exponent
 // field.  off + b <= 254, so the add never carries into the sign bit.
-__device__ __forceinline__ void decode16(uint4 h, uint2 l, uint32_t bb2, uint32_t d[8]) {
-  const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-  const uint32_t l0 = l.x, l1 = l.y;
-  const uint32_t l0s = l.x << 4, l1s = l.y << 4;
+__device__ __forceinline__ void decode8(uint2 hw, uint32_t l, uint32_t bb2, uint32_t d[4]) {
+  const uint32_t h2[2] = {hw.x, hw.y};
+  const uint32_t ls = l << 4;
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t src_lo = (p < 4) ? ((p & 2) ? l0s : l0) : ((p & 2) ? l1s : l1);
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t src_lo = (p & 2) ? ls : l;
     const uint32_t sel = (p & 1) ? 0x07030602u : 0x05010400u;
-    uint32_t x = __builtin_amdgcn_perm(hw[p >> 1], src_lo, sel);
+    uint32_t x = __builtin_amdgcn_perm(h2[p >> 1], src_lo, sel);
     x = ashr16x2(x, 4) & 0x87FF87FFu;
     d[p] = add16x2(x, bb2);
   }
 }
 
+// The 16 weights of one row of one chunk: its two halves.
+__device__ __forceinline__ void decode16(uint4 h, uint2 l, uint32_t bb2, uint32_t d[8]) {
+  decode8(make_uint2(h.x, h.y), l.x, bb2, d);
+  decode8(make_uint2(h.z, h.w), l.y, bb2, d + 4);
+}
+
 __device__ __forceinline__ uint32_t base_pair(uint32_t b) { return (b << 7) | (b << 23); }
 
-// Overwrite weight `pos` (0..15, may differ per lane) of a decoded chunk with `bits`.
-__device__ __forceinline__ void patch16(uint32_t d[8], uint32_t pos, uint32_t bits) {
+// Overwrite weight `pos` (0..2W-1, may differ per lane) of W decoded BF16 pairs with `bits`.
+template <int W>
+__device__ __forceinline__ void patch_pairs(uint32_t d[W], uint32_t pos, uint32_t bits) {
   const uint32_t v2 = bits | (bits << 16);
   const uint32_t hm = (pos & 1u) ? 0xFFFF0000u : 0x0000FFFFu;
   const uint32_t pi = pos >> 1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < W; ++i) {
     const uint32_t m = (pi == (uint32_t)i) ? hm : 0u;
     d[i] = (d[i] & ~m) | (v2 & m);
   }
 }
+__device__ __forceinline__ void patch16(uint32_t d[8], uint32_t pos, uint32_t bits) { patch_pairs<8>(d, pos, bits); }
 
 // First index in esc[lo, hi) whose k field is >= k0 (escapes ascend in k inside a channel).
 __device__ __forceinline__ uint32_t lower_bound_k(const uint32_t* __restrict__ esc, uint32_t lo, uint32_t hi,

@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "w12_device.h"
+#include "w12_gemm_common.h"
 #include "w12_kernels.h"
 
 namespace w12 {
@@ -38,11 +39,8 @@ constexpr int kSubRanges = kWaves * 4;
 constexpr int kUnitChunks = kSubRanges;   // chunks per stream-K unit (one per sub-range)
 constexpr int kRB = 4;                    // row blocks per tile (64 rows)
 constexpr int kTileRows = kRB * kRowsPerBlock;
-constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past any plane: reads give 0, writes are dropped
-constexpr int kCachePolicySc1 = 16;             // buffer access cache policy: sc1 (device coherent)
 
 __device__ __forceinline__ int64_t split_point(int64_t total, int64_t parts, int64_t q) { return q * total / parts; }
-__device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct GemmArgs {
   const uint16_t* X;
@@ -67,22 +65,6 @@ struct GemmArgs {
   float* P;             // [2G][tile elements] partial tiles
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// The wave's index in the work-group, known to be uniform (scalar).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
-}
-// 16 bytes per lane from the buffer into LDS: lane i's bytes land at dst + 16 i.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
-}
-
 // ------------------------------------------------------------------------------------------
 // Reading the ring.  The compiler's waits for buffer-to-LDS loads model each DMA as a 16-byte
 // write at its base address (the wave actually writes 16 bytes per lane), so it can miss a
@@ -90,9 +72,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint3
 // instructions the compiler does not associate with the DMA, after an explicit vmcnt wait
 // for the stage: all other memory traffic stays under the compiler's own accounting.
 // ------------------------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) const uint8_t lds_u8;
-__device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
-
 // Batched LDS reads with literal offsets, one statement and one wait each (no register still
 // in flight is ever visible to the compiler).
 // M dwords 256 bytes apart (GEMV partials: one channel, M rows of X, red laid out [m][64]).
@@ -137,12 +116,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_write_u128(uint32_t a, uint4 v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};   // a native vector: asm inputs cannot be structs
   asm volatile("ds_write_b128 %0, %1" : : "v"(a), "v"(w) : "memory");
-}
-
-// Wait until at most N vector-memory instructions of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // One stage's LDS reads and the wait for them in a single statement, so no register holding
@@ -462,22 +435,6 @@ struct MfmaPath {
 // before it bumps any counter.  Agent-scope release/acquire fences would write back /
 // invalidate the whole L2 of the XCD instead.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-// A barrier without the memory fence of __syncthreads (whose release part would wait for
-// every buffer-to-LDS load in flight); LDS writes are waited for explicitly before it.
-__device__ __forceinline__ void barrier() { __builtin_amdgcn_s_barrier(); }
-
-__device__ __forceinline__ uint4 lds_read_u128(uint32_t a) {
-  uint4 v;
-  asm volatile("ds_read_b128 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
-__device__ __forceinline__ uint32_t lds_read_u32(uint32_t a) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1\ns_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
 
 // Stream-K bookkeeping: work-group w owns units [ubeg(w), ubeg(w+1)).
 __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w * g.units / g.G; }
@@ -538,20 +495,6 @@ __device__ __forceinline__ void issue_slice(__amdgpu_buffer_rsrc_t re, uint32_t 
   const int lane = threadIdx.x & 63;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)&slice[wave * kWave], 16,
                                            (int)((s0 + (uint32_t)(wave * kWave * 4 + lane * 4)) * 4u), 0, 0, 0);
-}
-
-// A global-memory escape entry, waited for on the spot.  The compiler cannot tell the two
-// escape modes apart at a cursor's later uses; a cursor register left with a load in flight
-// would make it wait for all vector-memory traffic (the ring's stages included) at every step.
-__device__ __forceinline__ uint32_t esc_global(const uint32_t* __restrict__ esc, uint32_t i) {
-  uint32_t v;
-  const uint32_t* p = esc + i;
-  asm volatile("global_load_dword %0, %1, off\n"
-               "s_waitcnt vmcnt(0)"
-               : "=v"(v)
-               : "v"(p)
-               : "memory");
-  return v;
 }
 
 struct LaneEsc {
@@ -988,27 +931,6 @@ __global__ __launch_bounds__(256) void k_pad_x(const uint16_t* __restrict__ X, i
 // ------------------------------------------------------------------------------------------
 // Planning and launch
 // ------------------------------------------------------------------------------------------
-static int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
-
-// Compute units of the current device (256 on MI355X; that value is also used when no device
-// is visible, so host-only planning gives the same sizes as on the GPU).
-static int device_cus() {
-  static std::once_flag once;
-  static int cus = 256;
-  std::call_once(once, [] {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      cus = v;
-    else
-      (void)hipGetLastError();
-  });
-  return cus;
-}
-
 // Resident work-groups per CU of one kernel variant, from the runtime occupancy calculator
 // (registers and LDS of the compiled kernel); when no device is visible, a conservative
 // estimate.  Cached per variant.
@@ -1061,20 +983,27 @@ static int groups_per_cu(int path, int M, int m_tile) {
 // for every M <= 16.  W12_GEMV_MAX_M (0..8) moves the boundary, e.g. 8 for the wavefront
 // reduction at every M <= 8.
 constexpr int kGemvMaxM = 2;
+// Smallest M that runs the wide tiles (W read once per 128 or 256 rows of X instead of once
+// per 64).  W12_WIDE_MIN_M moves it.
+constexpr int kWideMinM = 65;
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   GemmPlan p{};
   int gemv_max = env_int("W12_GEMV_MAX_M", kGemvMaxM);
   gemv_max = gemv_max < 0 ? 0 : (gemv_max > 8 ? 8 : gemv_max);
-  p.path = (M <= gemv_max) ? 1 : 2;
-  p.rb = kRB;
-  p.waves = kWaves;
+  const int wide_min = env_int("W12_WIDE_MIN_M", kWideMinM);
+  p.path = (M <= gemv_max) ? 1 : (M >= wide_min ? 3 : 2);
+  p.rb = p.path == 3 ? kWideRB : kRB;
+  p.waves = p.path == 3 ? kWideWaves : kWaves;
   const int64_t Nb = num_row_blocks(N);
   const int64_t Kc = num_chunks(K);
   p.row_groups = (Nb + p.rb - 1) / p.rb;
   if (p.path == 1) {
     p.m_tile = M;
     p.m_tiles = 1;
+  } else if (p.path == 3) {
+    p.m_tile = M <= 128 ? 128 : 256;
+    p.m_tiles = (M + p.m_tile - 1) / p.m_tile;
   } else {
     const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 48 ? 3 : 4));
     p.m_tile = 16 * mb;
@@ -1083,7 +1012,8 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   p.tiles = p.row_groups * p.m_tiles;
   p.upt = (Kc + kUnitChunks - 1) / kUnitChunks;
   p.units = p.tiles * p.upt;
-  int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", groups_per_cu(p.path, M, p.m_tile));
+  const int gpc = p.path == 3 ? wide_groups_per_cu(p.m_tile) : groups_per_cu(p.path, M, p.m_tile);
+  int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", gpc);
   const int max_grid = env_int("W12_MAX_GRID", 0);   // 0: no cap
   if (max_grid > 0 && G > max_grid) G = max_grid;
   if (G > p.units) G = p.units;
@@ -1168,6 +1098,7 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
     X = xp;
     ldx = kp;
   }
+  if (p.path == 3) return launch_gemm_wide(p, X, M, ldx, t, Y, ldy, ws, qpass, stream);
   a.X = X;
   a.ldx = ldx;
   a.base = t->base;

@@ -19,7 +19,7 @@ hipError_t launch_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, 
 hipError_t launch_unpack(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStream_t stream);
 
 struct GemmPlan {
-  int path;            // 1 = wavefront GEMV, 2 = MFMA tiles
+  int path;            // 1 = wavefront GEMV, 2 = MFMA tiles (streaming), 3 = wide MFMA tiles
   int splits;          // partial sums per tile (1 when a tile is never split)
   int rb;              // row blocks of 16 per tile
   int waves;           // waves per work-group (they split a segment's K range)
@@ -37,6 +37,14 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K);
+// The wide-tile path (many rows of X): 8 waves per work-group, tiles of 16 row blocks (256
+// channels) x m_tile (128 or 256) rows of X.
+constexpr int kWideWaves = 8;
+constexpr int kWideRB = 16;
+int wide_groups_per_cu(int m_tile);
+hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t,
+                            float* Y, int64_t ldy, void* ws, bool qpass, hipStream_t stream);
+
 hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream);
 // qpass: the Q pass on the nested 8-bit view (hi plane only, escapes exact)
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,

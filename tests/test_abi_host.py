@@ -115,23 +115,29 @@ def test_encode_decode_verify_validation():
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 512), (8, 5120, 17408), (16, 34816, 5120), (63, 7168, 5120),
-                                   (512, 34816, 5120), (9, 1, 16), (3, 17, 33)])
+                                   (512, 34816, 5120), (256, 5120, 17408), (100, 300, 4096), (70, 17, 33),
+                                   (9, 1, 16), (3, 17, 33)])
 def test_gemm_plan_is_consistent(m, n, k):
     p = w12.gemm_plan(m, n, k)
-    assert p["path"] == (1 if m <= 2 else 2)
+    assert p["path"] == (1 if m <= 2 else (2 if m < 65 else 3))
+    # streaming tiles: 4 row blocks (64 channels); wide tiles: 16 row blocks x 128 or 256 rows
+    rb = 16 if p["path"] == 3 else 4
+    assert p["rows_per_block"] == 16 * rb
+    if p["path"] == 3:
+        assert p["m_tile"] == (128 if m <= 128 else 256)
     assert p["splits"] >= 1
     kc = (k + 15) // 16
     upt = (kc + 15) // 16                       # stream-K units (16 chunks) per tile
-    tiles = ((n + 15) // 16 + 3) // 4 * ((m + p["m_tile"] - 1) // p["m_tile"])
+    tiles = ((n + 15) // 16 + rb - 1) // rb * ((m + p["m_tile"] - 1) // p["m_tile"])
     assert 1 <= p["grid"] <= tiles * upt       # never more work-groups than units
     assert p["counter_bytes"] % 256 == 0 and p["counter_bytes"] >= 4 * tiles
     if tiles <= p["grid"]:
         # a whole multiple of the tiles when that keeps 3/4 of the grid: no range crosses a tile
         assert p["grid"] % tiles == 0 or p["grid"] * 3 > 4 * (p["grid"] // tiles) * tiles
-    # counters + two partial tiles (64 rows x m tile) per work-group (+ X padded to whole
+    # counters + two partial tiles (tile channels x m tile) per work-group (+ X padded to whole
     # 16-k chunks when K is ragged)
     xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
-    assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * 64 * p["m_tile"] * 4 + xpad
+    assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * 16 * rb * p["m_tile"] * 4 + xpad
     assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]
 
 
@@ -144,6 +150,16 @@ def test_gemm_gemv_boundary_env(monkeypatch, limit):
         p = w12.gemm_plan(m, 4096, 4096)
         assert p["path"] == (1 if m <= eff else 2), (limit, m)
         assert p["m_tile"] == (m if p["path"] == 1 else 16)
+
+
+@pytest.mark.parametrize("limit", [3, 17, 65, 129, 100000])
+def test_gemm_wide_boundary_env(monkeypatch, limit):
+    """W12_WIDE_MIN_M moves the streaming / wide-tile boundary at each call."""
+    monkeypatch.setenv("W12_WIDE_MIN_M", str(limit))
+    for m in (3, 16, 64, 65, 100, 128, 129, 256, 512):
+        p = w12.gemm_plan(m, 5120, 5120)
+        assert p["path"] == (3 if m >= limit else 2), (limit, m)
+        assert p["m_tile"] == ((128 if m <= 128 else 256) if m >= limit else min(64, (m + 15) // 16 * 16))
 
 
 @pytest.mark.parametrize("cap", [1, 3, 100])
