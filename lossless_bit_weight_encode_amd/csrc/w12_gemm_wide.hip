@@ -55,12 +55,12 @@ struct WideArgs {
   const uint32_t* esc;
   uint32_t num_esc;
   int32_t M, N, K;
-  int64_t Kc, Nb;
+  int32_t Kc, Nb;
   int32_t MT;           // m tiles
-  int64_t tiles;        // row groups x m tiles
-  int64_t upt;          // units per tile
-  int64_t units;        // tiles x upt
-  int64_t G;            // work-groups
+  int32_t tiles;        // row groups x m tiles
+  int32_t upt;          // units per tile
+  int32_t units;        // tiles x upt
+  int32_t G;            // work-groups
   uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
@@ -85,7 +85,7 @@ struct WideCfg {
   static constexpr int kF4 = 8 * TM;                    // float4 groups of accumulators per lane
 };
 
-__device__ __forceinline__ int64_t wubeg(const WideArgs& g, int64_t w) { return w * g.units / g.G; }
+__device__ __forceinline__ int64_t wubeg(const WideArgs& g, int64_t w) { return w * (int64_t)g.units / g.G; }
 
 // A segment: the stretch of one tile inside a work-group's unit range.
 struct WSeg {
@@ -110,35 +110,45 @@ __device__ __forceinline__ void wseg(const WideArgs& g, int64_t u, int64_t u_end
   s.nst = (s.cs1 - s.cs0 + 1) / 2;
 }
 
-// Stage j of segment s into st: this wave's X fragments, hi row blocks 2 wave and 2 wave + 1,
-// and (waves 0-3) lo row blocks 4 wave .. 4 wave + 3.  A chunk past the segment reads X as
-// zero; its records are whatever follows (finite values times zero).
-template <int TM, bool kQ>
-__device__ __forceinline__ void wide_issue(const WideArgs& g, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rh,
-                                           __amdgpu_buffer_rsrc_t rl, const WSeg& s, uint32_t j, WideStage<TM>* st,
-                                           int wave, int lane) {
-  const uint32_t c = s.cs0 + 2 * j;
+// Per-lane DMA byte offsets of a segment's stage 0 (stage j adds j times 64, 512 and 256
+// bytes: two chunks of X, hi and lo); kOutOfRange for rows past M or row blocks past N.
+struct WDma {
+  uint32_t x[2];     // this wave's X fragments (at most 2 per stage)
+  uint32_t xkk[2];   // their chunk within the stage
+  uint32_t h, l;
+};
+
+template <int TM>
+__device__ __forceinline__ void wdma_setup(const WideArgs& g, const WSeg& s, int wave, int lane, WDma& d) {
 #pragma unroll
   for (int i = 0; i < WideCfg<TM>::kXDma; ++i) {
     const int f = wave * WideCfg<TM>::kXDma + i;
     const int kk = f / (2 * TM), mb = f % (2 * TM);
     const int m = s.mrow0 + 32 * mb + (lane & 31);
-    const uint32_t ck = c + (uint32_t)kk;
-    const bool ok = m < g.M && ck < s.cs1;
-    const uint32_t off =
-        ok ? (uint32_t)(((int64_t)m * g.ldx + (int64_t)ck * kChunkK + 8 * (lane >> 5)) * 2) : kOutOfRange;
-    dma16(rx, &st->x[f][0], off);
+    d.x[i] = m < g.M ? (uint32_t)(((int64_t)m * g.ldx + (int64_t)(s.cs0 + kk) * kChunkK + 8 * (lane >> 5)) * 2)
+                     : kOutOfRange;
+    d.xkk[i] = (uint32_t)kk;
   }
-  {
-    const int64_t rbg = s.rg * kWRB + 2 * wave + (lane >> 5);
-    const uint32_t off = rbg < g.Nb ? (uint32_t)(hi_offset(rbg, c, g.Kc, 0) + 16 * (lane & 31)) : kOutOfRange;
-    dma16(rh, &st->hi[2 * wave][0][0], off);
+  const int64_t rbh = s.rg * kWRB + 2 * wave + (lane >> 5);
+  d.h = rbh < g.Nb ? (uint32_t)(hi_offset(rbh, s.cs0, g.Kc, 0) + 16 * (lane & 31)) : kOutOfRange;
+  const int64_t rbl = s.rg * kWRB + 4 * (wave & 3) + (lane >> 4);
+  d.l = rbl < g.Nb ? (uint32_t)(lo_offset(rbl, s.cs0, g.Kc, 0) + 16 * (lane & 15)) : kOutOfRange;
+}
+
+// Stage j into st: this wave's X fragments, hi row blocks 2 wave and 2 wave + 1, and (waves
+// 0-3) lo row blocks 4 wave .. 4 wave + 3.  A chunk past the segment (nch chunks) reads X as
+// zero; its records are whatever follows (finite values times zero).
+template <int TM, bool kQ>
+__device__ __forceinline__ void wide_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rh,
+                                           __amdgpu_buffer_rsrc_t rl, const WDma& d, uint32_t j, uint32_t nch,
+                                           WideStage<TM>* st, int wave) {
+#pragma unroll
+  for (int i = 0; i < WideCfg<TM>::kXDma; ++i) {
+    const bool ok = d.x[i] != kOutOfRange && 2 * j + d.xkk[i] < nch;
+    dma16(rx, &st->x[wave * WideCfg<TM>::kXDma + i][0], ok ? d.x[i] + 64u * j : kOutOfRange);
   }
-  if (!kQ && wave < 4) {
-    const int64_t rbg = s.rg * kWRB + 4 * wave + (lane >> 4);
-    const uint32_t off = rbg < g.Nb ? (uint32_t)(lo_offset(rbg, c, g.Kc, 0) + 16 * (lane & 15)) : kOutOfRange;
-    dma16(rl, &st->lo[4 * wave][0][0], off);
-  }
+  dma16(rh, &st->hi[2 * wave][0][0], d.h != kOutOfRange ? d.h + 512u * j : kOutOfRange);
+  if (!kQ && wave < 4) dma16(rl, &st->lo[4 * wave][0][0], d.l != kOutOfRange ? d.l + 256u * j : kOutOfRange);
 }
 
 // Wait until stage j has landed for this wave: at most n newer stages (V DMAs each) remain.
@@ -306,7 +316,10 @@ void k_gemm_wide(WideArgs g) {
                                                (int)((s0 + (uint32_t)(wave * kWave * 4 + lane * 4)) * 4u), 0, 0, 0);
     }
     // ---- the first NS - 1 stages ----
-    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(g, rx, rh, rl, s, j, &ring[j], wave, lane);
+    WDma dm;
+    wdma_setup<TM>(g, s, wave, lane, dm);
+    const uint32_t nch = s.cs1 - s.cs0;
+    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave);
     wait_vm_all();
     barrier();
     WEsc cur[2];
@@ -321,8 +334,9 @@ void k_gemm_wide(WideArgs g) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][nb][r] = 0.f;
 
-    uint32_t slot = 0;          // ring slot of stage j
+    uint32_t slot = 0;   // ring slot of stage j
     for (uint32_t j = 0; j < s.nst; ++j) {
+      // stage j has landed once at most min(NS - 2, stages after it) newer stages remain
       const uint32_t left = s.nst - 1 - j;
       const uint32_t newer = left < (uint32_t)(NS - 2) ? left : (uint32_t)(NS - 2);
       if (wave < 4) wait_newer<V_LO, NS - 2>(newer);
@@ -330,8 +344,13 @@ void k_gemm_wide(WideArgs g) {
       barrier();   // stage j visible to all waves; every wave is done with stage j - 1
       if (j + NS - 1 < s.nst) {
         const uint32_t ws = slot == 0 ? NS - 1 : slot - 1;
-        wide_issue<TM, kQ>(g, rx, rh, rl, s, j + NS - 1, &ring[ws], wave, lane);
+        wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave);
       }
+      // one test per stage: does any lane of the wave hold an escape before the stage's end?
+      const uint32_t kend = (s.cs0 + 2 * j + 2) * kChunkK;
+      const bool pend = (cur[0].pos < cur[0].end && (cur[0].e >> 16) < kend) ||
+                        (cur[1].pos < cur[1].end && (cur[1].e >> 16) < kend);
+      const bool any_esc = __builtin_amdgcn_ballot_w64(pend) != 0;
       const uint32_t so = slot * kStageBytes;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -343,7 +362,7 @@ void k_gemm_wide(WideArgs g) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) decode8(h[nb], l[nb], bb2[nb], d[nb]);
         const uint32_t ck = s.cs0 + 2 * j + kk;
-        if (ck < s.cs1) {
+        if (any_esc && ck < s.cs1) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
             wesc_apply(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb], in_lds, slice_addr);
@@ -404,30 +423,39 @@ void k_gemm_wide(WideArgs g) {
       }
       __syncthreads();
       if (s_last) {
-        // the last arriver: sum the tile's partials in work-group order and write Y
+        // the last arriver: sum the tile's partials in work-group order and write Y.  Per
+        // contributor, the loads of 8 of this thread's float4 groups are in flight at once.
         const int pos_a = wubeg(g, w_a) < t0 ? 1 : 0;
+        constexpr int HG = 8;   // float4 groups per batch
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int half = 0; half < C::kF4 / HG; ++half) {
+          f32x4 v[HG];
+          for (int64_t jj = 0; jj < ns; ++jj) {
+            const int64_t sl = 2 * (w_a + jj) + (jj == 0 ? pos_a : 0);
+            const uint32_t sbase = (uint32_t)(sl * C::kTile);
+            f32x4 pv[HG];
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int grp = (i * 2 + nb) * 4 + q;
-              f32x4 v = {0.f, 0.f, 0.f, 0.f};
-              for (int64_t jj = 0; jj < ns; ++jj) {
-                const int64_t sl = 2 * (w_a + jj) + (jj == 0 ? pos_a : 0);
-                const uint32_t off = ((uint32_t)(sl * C::kTile) + (uint32_t)(grp * kWThreads + (int)threadIdx.x) * 4u) * 4u;
-                const f32x4 pv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, (int)off, 0, kCachePolicySc1));
-                v = (jj == 0) ? pv : v + pv;
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int m = s.mrow0 + out_row<TM>(wm, i, 4 * q + e, lane);
-                const int64_t n = s.n0 + out_col(wn, nb, lane);
-                const uint32_t off = (m < g.M && n < g.N) ? (uint32_t)(((int64_t)m * g.ldy + n) * 4) : kOutOfRange;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[e]), ry, (int)off, 0, 0);
-              }
+            for (int x = 0; x < HG; ++x) {
+              const int grp = half * HG + x;
+              const uint32_t off = (sbase + (uint32_t)(grp * kWThreads + (int)threadIdx.x) * 4u) * 4u;
+              pv[x] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rpart, (int)off, 0, kCachePolicySc1));
             }
+#pragma unroll
+            for (int x = 0; x < HG; ++x) v[x] = (jj == 0) ? pv[x] : v[x] + pv[x];
+          }
+#pragma unroll
+          for (int x = 0; x < HG; ++x) {
+            const int grp = half * HG + x;
+            const int i = grp / 8, nb = (grp / 4) % 2, q = grp % 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int m = s.mrow0 + out_row<TM>(wm, i, 4 * q + e, lane);
+              const int64_t n = s.n0 + out_col(wn, nb, lane);
+              const uint32_t off = (m < g.M && n < g.N) ? (uint32_t)(((int64_t)m * g.ldy + n) * 4) : kOutOfRange;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[x][e]), ry, (int)off, 0, 0);
+            }
+          }
+        }
         if (threadIdx.x == 0) __hip_atomic_store(g.counters + s.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -462,7 +490,7 @@ int wide_groups_per_cu(int m_tile) { return m_tile <= 128 ? occupancy_wide<2>(1)
 hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t,
                             float* Y, int64_t ldy, void* ws, bool qpass, hipStream_t stream) {
   WideArgs a;
-  a.Kc = num_chunks(t->K);
+  a.Kc = (int32_t)num_chunks(t->K);
   a.X = X;
   a.ldx = ldx;
   a.base = t->base;
@@ -474,12 +502,12 @@ hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int
   a.M = M;
   a.N = t->N;
   a.K = t->K;
-  a.Nb = num_row_blocks(t->N);
+  a.Nb = (int32_t)num_row_blocks(t->N);
   a.MT = p.m_tiles;
-  a.tiles = p.tiles;
-  a.upt = p.upt;
-  a.units = p.units;
-  a.G = p.grid;
+  a.tiles = (int32_t)p.tiles;
+  a.upt = (int32_t)p.upt;
+  a.units = (int32_t)p.units;
+  a.G = (int32_t)p.grid;
   const uint64_t chunks = (uint64_t)a.Nb * (uint64_t)a.Kc;
   a.hi_bytes = (uint32_t)(chunks * kHiChunkBytes);
   a.lo_bytes = (uint32_t)(chunks * kLoChunkBytes);
