@@ -286,6 +286,29 @@ def main():
                 log(f"[bench] {nm} M={m}: {t * 1e3:.1f} us, {ab / t / 1e6:.0f} GB/s moved")
         out["tree_sweep"] = sweep
 
+    # ---- batched verify on gate_up and down (MFMA-bound tiles) ----
+    if not args.no_sweep:
+        batched = {}
+        for nm in ("gate_up", "down"):
+            n, k = S.LAYER_SHAPES[nm]
+            for m in S.BATCHED_M:
+                x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
+                y = torch.empty(m, n, dtype=torch.float32, device=dev)
+                wsm = w12.gemm_workspace(m, n, k)
+                for i in range(3):
+                    w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm)
+                t = timed(lambda i: w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm), 10, stream)
+                fl = byte_floor_us(n, k, m, enc[nm].num_escapes)
+                plan = w12.gemm_plan(m, n, k)
+                batched[f"{nm}_M{m}"] = {
+                    "us": round(t * 1e3, 2), "TFLOPs": round(2 * m * n * k / t / 1e9, 1),
+                    "frac_of_bf16_peak": round(2 * m * n * k / t / 1e9 / BF16_PEAK_TFLOPS, 4),
+                    "weight_GBps": round(2 * n * k / t / 1e6, 1), "byte_floor_us": round(fl, 2),
+                    "floor_over_time": round(fl / (t * 1e3), 4), "kernel": kernel_name(plan, m),
+                }
+                log(f"[bench] batched {nm} M={m}: {t * 1e3:.1f} us, {2 * m * n * k / t / 1e9:.0f} TFLOP/s")
+        out["batched_verify"] = batched
+
     # ---- practical HBM ceilings measured with plain torch kernels (context for frac) ----
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     bcp = torch.empty_like(a)
@@ -388,10 +411,12 @@ def summarize_mfma(pmc_csv, probe_json):
 
 
 def kernel_name(plan, m):
-    """Name of the GEMM kernel variant a plan launches, as rocprofv3 lists it."""
+    """Name of the GEMM kernel variant a plan launches (exact pass), as rocprofv3 lists it."""
     if plan["path"] == 1:
-        return f"w12::k_gemm<w12::GemvPath<{m}>>"
-    return f"w12::k_gemm<w12::MfmaPath<{plan['m_tile'] // 16}>>"
+        return f"w12::k_gemm<w12::GemvPath<{m}>, false>"
+    if plan["path"] == 3:
+        return f"w12::k_gemm_wide<{plan['m_tile'] // 64}, false>"
+    return f"w12::k_gemm<w12::MfmaPath<{plan['m_tile'] // 16}>, false>"
 
 
 def traffic_from_profile(alg):

@@ -33,8 +33,6 @@
 
 namespace w12 {
 
-namespace {
-
 constexpr int kWWaves = kWideWaves;              // 8
 constexpr int kWThreads = kWWaves * kWave;       // 512
 constexpr int kWRB = kWideRB;                    // 16 row blocks
@@ -466,7 +464,7 @@ void k_gemm_wide(WideArgs g) {
 }
 
 template <int TM, bool kQ = false>
-int occupancy_wide(int fallback) {
+static int occupancy_wide(int fallback) {
   static std::once_flag once;
   static int v = 0;
   std::call_once(once, [fallback] {
@@ -482,8 +480,6 @@ int occupancy_wide(int fallback) {
   });
   return v;
 }
-
-}  // namespace
 
 int wide_groups_per_cu(int m_tile) { return m_tile <= 128 ? occupancy_wide<2>(1) : occupancy_wide<4>(1); }
 
