@@ -190,6 +190,35 @@ __device__ __forceinline__ void read_stage_wx(uint32_t ah, uint32_t al, uint32_t
   }
 }
 
+// The W reads plus the MFMA X operands of MB 16-row blocks: halves at +0 / +16 bytes, blocks
+// 2 KB apart.
+template <int MB>
+__device__ __forceinline__ void read_stage_wmx(uint32_t ah, uint32_t al, uint32_t ax, uint4 h[4], uint2 l[4],
+                                               uint4 xa[MB], uint4 xb[MB]) {
+  static_assert(MB >= 1 && MB <= 4, "MFMA row blocks");
+  if constexpr (MB == 1) {
+    asm volatile(W12_W_READS W12_X2(8, 0) W12_X2(9, 16) "s_waitcnt lgkmcnt(0)"
+                 : W12_W_OUTS(h, l), "=&v"(xa[0]), "=&v"(xb[0])
+                 : [ah] "v"(ah), [al] "v"(al), [ax] "v"(ax) : "memory");
+  } else if constexpr (MB == 2) {
+    asm volatile(W12_W_READS W12_X2(8, 0) W12_X2(9, 16) W12_X2(10, 2048) W12_X2(11, 2064) "s_waitcnt lgkmcnt(0)"
+                 : W12_W_OUTS(h, l), "=&v"(xa[0]), "=&v"(xb[0]), "=&v"(xa[1]), "=&v"(xb[1])
+                 : [ah] "v"(ah), [al] "v"(al), [ax] "v"(ax) : "memory");
+  } else if constexpr (MB == 3) {
+    asm volatile(W12_W_READS W12_X2(8, 0) W12_X2(9, 16) W12_X2(10, 2048) W12_X2(11, 2064) W12_X2(12, 4096)
+                     W12_X2(13, 4112) "s_waitcnt lgkmcnt(0)"
+                 : W12_W_OUTS(h, l), "=&v"(xa[0]), "=&v"(xb[0]), "=&v"(xa[1]), "=&v"(xb[1]), "=&v"(xa[2]),
+                   "=&v"(xb[2])
+                 : [ah] "v"(ah), [al] "v"(al), [ax] "v"(ax) : "memory");
+  } else {
+    asm volatile(W12_W_READS W12_X2(8, 0) W12_X2(9, 16) W12_X2(10, 2048) W12_X2(11, 2064) W12_X2(12, 4096)
+                     W12_X2(13, 4112) W12_X2(14, 6144) W12_X2(15, 6160) "s_waitcnt lgkmcnt(0)"
+                 : W12_W_OUTS(h, l), "=&v"(xa[0]), "=&v"(xb[0]), "=&v"(xa[1]), "=&v"(xb[1]), "=&v"(xa[2]),
+                   "=&v"(xb[2]), "=&v"(xa[3]), "=&v"(xb[3])
+                 : [ah] "v"(ah), [al] "v"(al), [ax] "v"(ax) : "memory");
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // LDS ring (per work-group; each wave owns its slice).  One object per stage lets the
 // compiler wait for exactly the stage being read.
@@ -331,19 +360,23 @@ struct GemvPath {
 };
 
 // MFMA tiles: MB m blocks of 16 rows; lane (r, g) supplies X row m0 + 16 mb + r of its own
-// chunk.  One block (up to 16 rows): X rides the LDS ring like W, so no register load is in
-// flight across a step and the compiler adds no waits of its own to the loop.  More blocks:
-// X is loaded one step ahead into registers (the LDS would not hold two work-groups per CU).
+// chunk.  X rides the LDS ring like W (2 KB per wave and block), so no register load is in
+// flight across a step and the compiler adds no waits of its own to the loop - except for
+// two blocks, whose X is loaded one step ahead into registers (with X in LDS the LDS would
+// not hold two work-groups per CU).
 template <int MB>
 struct MfmaPath {
   static constexpr int kMRows = MB * 16;
   static constexpr int kWavesPerEU = MB <= 2 ? 2 : 1;   // register budget: two work-groups per CU up to 32 rows
-  static constexpr bool kXInLds = MB == 1;
+  // X in LDS for 16 rows (two work-groups per CU fit) and for 48-64 rows (one per CU in any
+  // case: 5-7% faster than register X); 32-row tiles keep X in registers, which keeps two
+  // work-groups per CU (with X in LDS they would need 98 KB each)
+  static constexpr bool kXInLds = MB != 2;
   static constexpr int kVmemPerStage = 6 + 2 * MB;   // 6 W DMA + 2 MB X loads
   typedef f32x4 Acc;
   static constexpr int kAcc = MB;
   struct XLds {
-    uint4 x[kWaves][2 * kWave];   // per wave [lane group][row][half]: 32 bytes per (lane group, row)
+    uint4 x[kWaves][2 * MB * kWave];   // per wave [m block][lane group][row][half]: 32 bytes per (lane group, row)
   };
   struct XNone {};
   typedef typename std::conditional<kXInLds, XLds, XNone>::type XStage;
@@ -352,21 +385,26 @@ struct MfmaPath {
     q0 = wave * 4 + (lane >> 5);
     q1 = q0 + 2;
   }
-  // X load d, lane l: row m0 + (l / 2) % 16, half l % 2 of lane group 2d + l / 32; lane l of a
-  // load lands at 16 l, i.e. at (lane group, row, half) = ((l / 32 + 2d) * 16 + row) * 32 + 16 half
+  // X load (mb, d), lane l: row m0 + 16 mb + (l / 2) % 16, half l % 2 of lane group 2d + l / 32;
+  // lane l of a load lands at 16 l of block mb's 2 KB, i.e. at (lane group, row, half) =
+  // ((l / 32 + 2d) * 16 + row) * 32 + 16 half
   __device__ static void issue_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, const uint32_t xc0[2],
                                  const uint32_t xc_end[2], uint32_t stride, int m0, uint32_t j, XStage* xs,
                                  int wave) {
     if constexpr (kXInLds) {
       const int lane = threadIdx.x & 63;
-      const uint32_t m = (uint32_t)(m0 + ((lane >> 1) & 15)), half = lane & 1;
+      const uint32_t half = lane & 1;
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const uint32_t c = xc0[d] + stride * j;
-        const uint32_t off = (m < (uint32_t)g.M && c < xc_end[d])
-                                 ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
-                                 : kOutOfRange;
-        dma16(rx, &xs->x[wave][d * kWave], off);
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t m = (uint32_t)(m0 + mb * 16 + ((lane >> 1) & 15));
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t c = xc0[d] + stride * j;
+          const uint32_t off = (m < (uint32_t)g.M && c < xc_end[d])
+                                   ? (m * (uint32_t)g.ldx + c * kChunkK) * 2u + half * 16u
+                                   : kOutOfRange;
+          dma16(rx, &xs->x[wave][(mb * 2 + d) * kWave], off);
+        }
       }
     }
   }
@@ -376,7 +414,7 @@ struct MfmaPath {
   }
   __device__ static void read_stage(uint32_t ah, uint32_t al, const XStage* xs, int wave, uint4 h[4], uint2 l[4],
                                     uint4 xa[MB], uint4 xb[MB]) {
-    if constexpr (kXInLds) read_stage_wx<1>(ah, al, x_addr(xs, wave), h, l, xa, xb);
+    if constexpr (kXInLds) read_stage_wmx<MB>(ah, al, x_addr(xs, wave), h, l, xa, xb);
     else read_stage_w(ah, al, h, l);
   }
   __device__ static void load_x(const GemmArgs& g, __amdgpu_buffer_rsrc_t rx, int m0, uint32_t c, bool ok, uint4 xa[MB],
