@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-full-model", action="store_true", help="skip the 64-layer weight stream")
+    ap.add_argument("--model-layers", type=int, default=S.FULL_MODEL_LAYERS)
     ap.add_argument("--only-layer", action="store_true", help="time only the layer steps (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the layer steps, run one torch elementwise kernel that reads and writes exactly "
@@ -309,6 +311,12 @@ def main():
                 log(f"[bench] batched {nm} M={m}: {t * 1e3:.1f} us, {2 * m * n * k / t / 1e9:.0f} TFLOP/s")
         out["batched_verify"] = batched
 
+    # ---- full-model weight stream: 64 layers resident, 256 GEMMs at M=32 from cold weights ----
+    if not args.no_full_model:
+        del copies
+        torch.cuda.empty_cache()
+        out["full_model"] = full_model_leg(dev, stream, args.model_layers, 32)
+
     # ---- practical HBM ceilings measured with plain torch kernels (context for frac) ----
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     bcp = torch.empty_like(a)
@@ -408,6 +416,82 @@ def summarize_mfma(pmc_csv, probe_json):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def full_model_leg(dev, stream, n_layers, m, reps=5):
+    """The full-model weight stream: n_layers decoder layers (each drawn from its own seed on
+    the GPU's generator, see w12_synth.layer_device), encoded and checked bit for bit at load
+    time, then all 4 n_layers GEMMs launched back to back at M=m.  Before every timed pass a
+    1 GiB buffer is written, so the pass starts from cold weights (the W12 model is far larger
+    than the 256 MB Infinity Cache in any case)."""
+    names = list(S.LAYER_ORDER)
+    model, res = [], torch.zeros(n_layers, len(names), 2, dtype=torch.int64, device=dev)
+    t_enc = t_ver = 0.0
+    wbytes = 0
+    for li in range(n_layers):
+        lay = S.layer_device(li, dev)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        enc = {nm: w12.encode(lay[nm], stream=stream) for nm in names}
+        e1.record(stream)
+        for i, nm in enumerate(names):
+            w12.verify_async(enc[nm], lay[nm], res[li, i], stream=stream)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        t_enc += e0.elapsed_time(e1)
+        t_ver += e1.elapsed_time(e2)
+        wbytes += sum(2 * lay[nm].numel() for nm in names)
+        model.append(enc)
+        del lay
+    bad = int(res[:, :, 0].sum().item())
+    assert bad == 0, f"full-model load-time check: {bad} mismatching weights"
+    torch.cuda.empty_cache()
+    escapes = sum(enc[nm].num_escapes for enc in model for nm in names)
+    w12_bytes = sum(enc[nm].nbytes() for enc in model for nm in names)
+    log(f"[bench] full model: {n_layers} layers, {w12_bytes / 1e9:.2f} GB W12, encode {t_enc:.1f} ms, "
+        f"verify {t_ver:.1f} ms")
+
+    xs = {k: dev_bits(S.activations(m, k, S.x_seed(m, k))) for k in {S.LAYER_SHAPES[nm][1] for nm in names}}
+    ys = {nm: torch.empty(m, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names}
+    wss = {nm: w12.gemm_workspace(m, *S.LAYER_SHAPES[nm]) for nm in names}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        for enc in model:
+            for nm in names:
+                w12.gemm(xs[S.LAYER_SHAPES[nm][1]], enc[nm], y=ys[nm], ws=wss[nm], stream=stream)
+
+    one_pass()   # warm-up (code objects, first-touch of the outputs)
+    times = []
+    for _ in range(reps):
+        flush.fill_(reps)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        one_pass()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    t = float(np.median(times))
+    moved = sum(alg_bytes(enc[nm].n, enc[nm].k, m, enc[nm].num_escapes) for enc in model for nm in names)
+    log(f"[bench] full model GEMM pass M={m}: {t:.3f} ms, {wbytes / t / 1e6:.0f} weight-GB/s, "
+        f"{moved / t / 1e6:.0f} GB/s moved")
+    out = {
+        "what": f"{n_layers} decoder layers (4 GEMMs each) resident in HBM, all {4 * n_layers} GEMMs launched "
+                f"back to back at M={m} from cold weights; weights drawn on the GPU generator",
+        "layers": n_layers, "M": m, "weights_bf16_bytes": wbytes, "w12_bytes": w12_bytes, "escapes": escapes,
+        "bits_per_weight": round(w12_bytes * 8 / (wbytes / 2), 5),
+        "gemm_pass_ms_median": round(t, 4), "gemm_pass_ms_min": round(min(times), 4), "reps": reps,
+        "weight_GBps": round(wbytes / t / 1e6, 1), "bytes_moved_GBps": round(moved / t / 1e6, 1),
+        "bytes_moved_frac_of_8TBps": round(moved / t / 1e6 / HBM_PEAK_GBPS, 4),
+        "encode_ms": round(t_enc, 3), "encode_GBps": round(wbytes / t_enc / 1e6, 1),
+        "verify_ms": round(t_ver, 3), "verify_GBps": round((1.75 * wbytes + 4 * escapes) / t_ver / 1e6, 1),
+    }
+    del model
+    torch.cuda.empty_cache()
+    return out
 
 
 def kernel_name(plan, m):

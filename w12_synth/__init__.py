@@ -6,7 +6,8 @@ and the HIP path receive the BF16 bit patterns produced here and nothing else.
 
 Every tensor is generated on the host with a seeded ``torch.Generator`` (CPU), so the
 bits do not depend on the GPU, and is returned as a numpy ``uint16`` array of raw
-BF16 bit patterns (row-major).  ``to_bf16`` rounds float32 to BF16 with
+BF16 bit patterns (row-major).  The one exception is ``layer_device``, the same layer
+recipe drawn on the GPU for the 64-layer timing run.  ``to_bf16`` rounds float32 to BF16 with
 round-to-nearest-even through ``torch.Tensor.to(torch.bfloat16)``.
 
 Recipes (the pages give no weights, so these stand in for the dense 27B-class
@@ -177,3 +178,28 @@ def random_bits_matrix(gen: np.random.Generator, n: int, k: int, kind: str = "ga
         w[gen.random((n, k)) < 0.01] = 0
         return w.astype(np.uint16)
     raise ValueError(kind)
+
+
+def layer_device(seed: int, device) -> dict:
+    """The layer recipe drawn on the GPU's own generator, for the full-model stream.
+
+    Same shapes, order and distributions as ``layer`` (Gaussian x per-channel lognormal(0, 0.5)
+    scale, round(1e-4 N K) exact zeros), but the bits come from the device generator, so they
+    differ from the host recipe's.  Drawing 64 layers on the host would take minutes; the
+    parity tests check sampled host-drawn layers of the same recipe.  Returns int16 tensors of
+    raw BF16 bits on ``device``.
+    """
+    gen = torch.Generator(device=device).manual_seed(seed)
+    out = {}
+    for name in LAYER_ORDER:
+        n, k = LAYER_SHAPES[name]
+        z = torch.randn(n, k, generator=gen, device=device)
+        s = torch.exp(0.5 * torch.randn(n, 1, generator=gen, device=device))
+        z.mul_(s).mul_(0.02)
+        w = z.to(torch.bfloat16).view(torch.int16)
+        del z
+        nz = int(round(1e-4 * n * k))
+        pos = torch.randint(0, n * k, (nz,), generator=gen, device=device)
+        w.view(-1)[pos] = 0
+        out[name] = w
+    return out
