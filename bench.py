@@ -245,6 +245,29 @@ def main():
     out["roofline"].update(traffic_from_profile(ab))
     out["load_time"] = load_leg
 
+    # ---- the same four products in one grouped launch (w12_gemm_group) ----
+    xs_g = [x_dev[(nm, m_step)] for nm in names]
+    ys_g = [y_dev[nm] for nm in names]
+    ws_g = w12.gemm_group_workspace(m_step, [enc[nm] for nm in names])
+
+    def group_step(i):
+        c = copies[i % len(copies)]
+        w12.gemm_group(xs_g, [c[nm] for nm in names], ys_g, ws=ws_g, stream=stream)
+
+    for i in range(args.warmup):
+        group_step(i)
+    torch.cuda.synchronize()
+    t_grp = timed(group_step, args.steps, stream)
+    out["grouped"] = {
+        "what": "the same four independent products (qkv, o_proj, gate_up, down at M=16) in one stream-K "
+                "launch (w12_gemm_group); valid where the products do not depend on one another",
+        "ms_per_step": round(t_grp, 5), "weight_GBps": round(weight_bytes / t_grp / 1e6, 1),
+        "bytes_moved_GBps": round(moved / t_grp / 1e6, 1),
+        "bytes_moved_frac_of_8TBps": round(moved / t_grp / 1e6 / HBM_PEAK_GBPS, 4),
+    }
+    log(f"[bench] grouped layer step {t_grp * 1e3:.1f} us -> {weight_bytes / t_grp / 1e6:.1f} weight-GB/s, "
+        f"{moved / t_grp / 1e6:.1f} GB/s moved")
+
     # ---- the Q pass (nested 8-bit view, hi plane only) of the same layer step ----
     def q_step(i):
         c = copies[i % len(copies)]
@@ -462,19 +485,36 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
             for nm in names:
                 w12.gemm(xs[S.LAYER_SHAPES[nm][1]], enc[nm], y=ys[nm], ws=wss[nm], stream=stream)
 
-    one_pass()   # warm-up (code objects, first-touch of the outputs)
-    times = []
-    for _ in range(reps):
-        flush.fill_(reps)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        one_pass()
-        b.record(stream)
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
+    # grouped: `per` layers (4 per products) per launch
+    per = 2
+    wsg = w12.gemm_group_workspace(m, [model[0][nm] for nm in names] * per)
+    xg = [xs[S.LAYER_SHAPES[nm][1]] for nm in names] * per
+    yg = [torch.empty(m, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names * per]
+
+    def grouped_pass():
+        for l0 in range(0, len(model), per):
+            ts = [model[l][nm] for l in range(l0, min(l0 + per, len(model))) for nm in names]
+            w12.gemm_group(xg[:len(ts)], ts, yg[:len(ts)], ws=wsg, stream=stream)
+
+    def time_pass(fn):
+        fn()   # warm-up (code objects, first-touch of the outputs)
+        times = []
+        for _ in range(reps):
+            flush.fill_(reps)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return times
+
+    times = time_pass(one_pass)
+    times_g = time_pass(grouped_pass)
     del flush
     t = float(np.median(times))
+    t_g = float(np.median(times_g))
     moved = sum(alg_bytes(enc[nm].n, enc[nm].k, m, enc[nm].num_escapes) for enc in model for nm in names)
     log(f"[bench] full model GEMM pass M={m}: {t:.3f} ms, {wbytes / t / 1e6:.0f} weight-GB/s, "
         f"{moved / t / 1e6:.0f} GB/s moved")
@@ -488,7 +528,14 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
         "bytes_moved_frac_of_8TBps": round(moved / t / 1e6 / HBM_PEAK_GBPS, 4),
         "encode_ms": round(t_enc, 3), "encode_GBps": round(wbytes / t_enc / 1e6, 1),
         "verify_ms": round(t_ver, 3), "verify_GBps": round((1.75 * wbytes + 4 * escapes) / t_ver / 1e6, 1),
+        "grouped": {
+            "what": f"the same {4 * n_layers} products, {4 * per} per launch (w12_gemm_group, {per} layers each)",
+            "gemm_pass_ms_median": round(t_g, 4), "gemm_pass_ms_min": round(min(times_g), 4),
+            "weight_GBps": round(wbytes / t_g / 1e6, 1), "bytes_moved_GBps": round(moved / t_g / 1e6, 1),
+            "bytes_moved_frac_of_8TBps": round(moved / t_g / 1e6 / HBM_PEAK_GBPS, 4),
+        },
     }
+    log(f"[bench] full model grouped pass M={m}: {t_g:.3f} ms, {moved / t_g / 1e6:.0f} GB/s moved")
     del model
     torch.cuda.empty_cache()
     return out

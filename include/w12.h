@@ -168,6 +168,37 @@ int w12_gemm(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
 int w12_gemm_q(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
                float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
 
+/*
+ * Grouped launch: several independent products of the same M in one launch (summary page
+ * method bullet of section 4.1: the W12 GEMM is a stream-K GEMM whose split is reduced in a
+ * fixed order).  items[i] asks for Y_i = X_i . W_i^T exactly as w12_gemm would (same operand
+ * layouts, pitches and alignment rules, the same tolerance); the launch streams the W12 records
+ * of all count products under one stream-K schedule over their concatenated work units, so the
+ * pipeline fill, the tail and the split-K fixups are paid once per launch rather than once per
+ * product.  Each Y_i is bitwise identical from run to run for the same (M, shapes, order of the
+ * items), though not in general bitwise equal to w12_gemm's result (the K split points differ).
+ * The products must not depend on one another: no Y_i may overlap any X_j or W_j of the group.
+ * Limits: 1 <= count <= W12_GROUP_MAX; 1 <= M <= 64; every K a multiple of 16.  Outside them
+ * the call returns W12_ERR_UNSUPPORTED_SHAPE.  items and the descriptors they point to are host
+ * memory read during the call only.  ws: at least w12_gemm_group_workspace_size bytes,
+ * initialised once with w12_gemm_workspace_init (counters at its start; every call leaves them
+ * zero).  W12_GEMV_MAX_M, W12_GROUPS_PER_CU and W12_MAX_GRID apply as for w12_gemm.
+ */
+#define W12_GROUP_MAX 8
+typedef struct w12_gemm_item {
+  const uint16_t *X;     /* BF16 [M][ldx], device                                          */
+  int64_t ldx;
+  const w12_tensor *t;   /* host descriptor of W_i (device planes)                         */
+  float *Y;              /* FP32 [M][ldy], device                                          */
+  int64_t ldy;
+} w12_gemm_item;
+int w12_gemm_group_workspace_size(int32_t M, int32_t count, const w12_gemm_item *items, uint64_t *bytes);
+int w12_gemm_group(int32_t M, int32_t count, const w12_gemm_item *items, void *ws, uint64_t ws_bytes,
+                   hipStream_t stream);
+/* The Q pass (as w12_gemm_q) of every product of a group, in one launch. */
+int w12_gemm_group_q(int32_t M, int32_t count, const w12_gemm_item *items, void *ws, uint64_t ws_bytes,
+                     hipStream_t stream);
+
 /* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
   int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles                       */

@@ -14,7 +14,11 @@ from ._lib import (  # noqa: F401
     encode,
     encode_count,
     encode_emit,
+    GROUP_MAX,
     gemm,
+    gemm_group,
+    gemm_group_workspace,
+    gemm_group_workspace_size,
     gemm_plan,
     gemm_workspace,
     gemm_workspace_init,

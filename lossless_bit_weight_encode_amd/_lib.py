@@ -29,6 +29,13 @@ class _Tensor(ctypes.Structure):
     ]
 
 
+class _GemmItem(ctypes.Structure):
+    _fields_ = [("X", _c_p), ("ldx", _c_i64), ("t", ctypes.POINTER(_Tensor)), ("Y", _c_p), ("ldy", _c_i64)]
+
+
+GROUP_MAX = 8
+
+
 class _PlanInfo(ctypes.Structure):
     _fields_ = [
         ("path", _c_i32), ("splits", _c_i32), ("rows_per_block", _c_i32), ("m_tile", _c_i32),
@@ -48,6 +55,9 @@ _SIGNATURES = {
     "w12_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
     "w12_gemm_q": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
     "w12_gemm_plan": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_PlanInfo)]),
+    "w12_gemm_group_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), ctypes.POINTER(_c_u64)]),
+    "w12_gemm_group": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), _c_p, _c_u64, _c_p]),
+    "w12_gemm_group_q": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), _c_p, _c_u64, _c_p]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
     "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w12_last_error": (ctypes.c_char_p, []),
@@ -280,3 +290,56 @@ def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch
 
 def bits_per_weight(n: int, k: int, e: int) -> float:
     return float(lib().w12_bits_per_weight(n, k, e))
+
+
+def _group_items(xs, ts, ys):
+    """ctypes item array for a group (the descriptors are kept alive alongside it)."""
+    n = len(ts)
+    descs = [t.descriptor() for t in ts]
+    items = (_GemmItem * max(n, 1))()
+    for i in range(n):
+        items[i].X = _ptr(xs[i])
+        items[i].ldx = _pitch(xs[i])
+        items[i].t = ctypes.pointer(descs[i])
+        items[i].Y = _ptr(ys[i])
+        items[i].ldy = _pitch(ys[i])
+    return items, descs
+
+
+def gemm_group_workspace_size(m: int, ts) -> int:
+    descs = [t.descriptor() for t in ts]
+    items = (_GemmItem * max(len(ts), 1))()
+    for i, d in enumerate(descs):
+        items[i].t = ctypes.pointer(d)
+    b = _c_u64()
+    _check("w12_gemm_group_workspace_size", lib().w12_gemm_group_workspace_size(m, len(ts), items, ctypes.byref(b)))
+    return b.value
+
+
+def gemm_group_workspace(m: int, ts, device="cuda", stream=None) -> torch.Tensor:
+    """A ready-to-use (zero-initialised) workspace for gemm_group() with M=m on the tensors ts."""
+    ws = torch.empty(gemm_group_workspace_size(m, ts), dtype=torch.uint8, device=device)
+    gemm_workspace_init(ws, stream)
+    return ws
+
+
+def gemm_group(xs, ts, ys=None, ws: torch.Tensor | None = None, stream=None, qpass: bool = False):
+    """Y_i = X_i @ W_i^T for independent products of one M in a single launch (w12_gemm_group,
+    or w12_gemm_group_q with qpass).  Returns the list of Y_i (FP32 [M, N_i])."""
+    if len(xs) != len(ts):
+        raise ValueError("one X per tensor")
+    _require_cuda(*xs)
+    for x in xs:
+        _bits16(x)
+    m = xs[0].shape[0] if xs else 0
+    if any(x.shape[0] != m for x in xs):
+        raise ValueError("every X of a group has the same number of rows")
+    if ys is None:
+        ys = [torch.empty(m, t.n, dtype=torch.float32, device=xs[0].device) for t in ts]
+    _require_cuda(*ys)
+    if ws is None:
+        ws = gemm_group_workspace(m, ts, xs[0].device, stream)
+    items, _descs = _group_items(xs, ts, ys)
+    name = "w12_gemm_group_q" if qpass else "w12_gemm_group"
+    _check(name, getattr(lib(), name)(m, len(ts), items, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return ys

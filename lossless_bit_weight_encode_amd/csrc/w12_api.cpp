@@ -64,6 +64,13 @@ int check_tensor(const w12_tensor* t) {
   return W12_OK;
 }
 
+// Prefix the current message with the index of the group item it concerns.
+int item_fail(int code, int i) {
+  char msg[sizeof(g_err)];
+  snprintf(msg, sizeof(msg), "%s", g_err);
+  return fail(code, "item %d: %s", i, msg);
+}
+
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W12_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -188,6 +195,72 @@ int w12_gemm(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, flo
 int w12_gemm_q(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy, void* ws,
                uint64_t ws_bytes, hipStream_t stream) {
   return gemm_call(X, M, ldx, t, Y, ldy, ws, ws_bytes, true, stream);
+}
+
+// Validates a group and plans it; on success fills tiles_of / upt_of and *plan.
+static int group_plan(int32_t M, int32_t count, const w12_gemm_item* items, w12::GemmPlan* plan, int64_t* tiles_of,
+                      int64_t* upt_of) {
+  if (count < 1 || count > W12_GROUP_MAX)
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "group of %d products outside 1..%d", count, W12_GROUP_MAX);
+  if (M < 1 || M > 64) return fail(W12_ERR_UNSUPPORTED_SHAPE, "grouped M=%d outside 1..64", M);
+  if (!items) return fail(W12_ERR_INVALID_ARG, "items is NULL");
+  int32_t N[W12_GROUP_MAX], K[W12_GROUP_MAX];
+  for (int i = 0; i < count; ++i) {
+    int rc = check_tensor(items[i].t);
+    if (rc) return item_fail(rc, i);
+    if (items[i].t->K % w12::kChunkK)
+      return fail(W12_ERR_UNSUPPORTED_SHAPE, "item %d: K=%d is not a multiple of 16", i, items[i].t->K);
+    N[i] = items[i].t->N;
+    K[i] = items[i].t->K;
+  }
+  *plan = w12::plan_gemm_group(M, count, N, K, tiles_of, upt_of);
+  return W12_OK;
+}
+
+int w12_gemm_group_workspace_size(int32_t M, int32_t count, const w12_gemm_item* items, uint64_t* bytes) {
+  w12::GemmPlan p;
+  int64_t tiles_of[W12_GROUP_MAX], upt_of[W12_GROUP_MAX];
+  int rc = group_plan(M, count, items, &p, tiles_of, upt_of);
+  if (rc) return rc;
+  if (!bytes) return fail(W12_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = p.ws_bytes;
+  return ok();
+}
+
+static int gemm_group_call(int32_t M, int32_t count, const w12_gemm_item* items, void* ws, uint64_t ws_bytes,
+                           bool qpass, hipStream_t stream) {
+  w12::GemmPlan p;
+  int64_t tiles_of[W12_GROUP_MAX], upt_of[W12_GROUP_MAX];
+  int rc = group_plan(M, count, items, &p, tiles_of, upt_of);
+  if (rc) return rc;
+  for (int i = 0; i < count; ++i) {
+    const w12_gemm_item& it = items[i];
+    if ((rc = check_bf16_matrix(it.X, it.ldx, it.t->K, "X"))) return item_fail(rc, i);
+    if (((int64_t)M - 1) * it.ldx + it.t->K + 16 >= (int64_t(1) << 30))
+      return fail(W12_ERR_UNSUPPORTED_SHAPE, "item %d: X spans too many elements for 31-bit buffer offsets", i);
+    if (!it.Y) return fail(W12_ERR_INVALID_ARG, "item %d: Y is NULL", i);
+    if (it.ldy < it.t->N) return fail(W12_ERR_INVALID_ARG, "item %d: Y pitch %lld < N", i, (long long)it.ldy);
+    if (((int64_t)M - 1) * it.ldy + it.t->N >= (int64_t(1) << 29))
+      return fail(W12_ERR_UNSUPPORTED_SHAPE, "item %d: Y spans too many elements for 31-bit buffer offsets", i);
+    if (!aligned(it.Y, 4)) return fail(W12_ERR_MISALIGNED, "item %d: Y must be 4-byte aligned", i);
+  }
+  if (ws_bytes < p.ws_bytes)
+    return fail(W12_ERR_WORKSPACE_TOO_SMALL, "workspace %llu bytes < %llu needed", (unsigned long long)ws_bytes,
+                (unsigned long long)p.ws_bytes);
+  if (!ws) return fail(W12_ERR_INVALID_ARG, "ws is NULL");
+  if (!aligned(ws, 16)) return fail(W12_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  return hip_status(w12::launch_gemm_group(p, M, count, items, tiles_of, upt_of, ws, qpass, stream),
+                    qpass ? "gemm_group_q" : "gemm_group");
+}
+
+int w12_gemm_group(int32_t M, int32_t count, const w12_gemm_item* items, void* ws, uint64_t ws_bytes,
+                   hipStream_t stream) {
+  return gemm_group_call(M, count, items, ws, ws_bytes, false, stream);
+}
+
+int w12_gemm_group_q(int32_t M, int32_t count, const w12_gemm_item* items, void* ws, uint64_t ws_bytes,
+                     hipStream_t stream) {
+  return gemm_group_call(M, count, items, ws, ws_bytes, true, stream);
 }
 
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {

@@ -56,14 +56,53 @@ struct GemmArgs {
   int32_t MT;           // m tiles
   int64_t tiles;        // row groups x m tiles
   int64_t upt;          // units per tile
-  int64_t units;        // tiles x upt
+  int64_t ubase;        // first unit of this product in the launch's unit space (0 unless grouped)
+  int64_t units;        // units of the whole launch (every product of a group)
   int64_t G;            // work-groups
   uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
-  uint32_t* counters;   // [tiles] arrival counters
-  float* P;             // [2G][tile elements] partial tiles
+  uint32_t* counters;   // [tiles] arrival counters of this product's tiles
+  float* P;             // [2G][tile elements] partial tiles (shared by a group)
 };
+
+// Several independent products of one launch (same M): work-group w takes units
+// [w U / G, (w+1) U / G) of their concatenated unit spaces, product i owning
+// [g[i].ubase, g[i].ubase + g[i].tiles * g[i].upt).  A single product is a group of one.
+constexpr int kGroupMax = 8;
+template <int NG>
+struct GroupArgs {
+  GemmArgs g[NG];
+  int32_t count;
+};
+
+// The product that owns unit u (uniform).
+template <int NG>
+__device__ __forceinline__ int gemm_of(const GroupArgs<NG>& ga, int64_t u) {
+  int gi = 0;
+  if constexpr (NG > 1) {
+#pragma unroll
+    for (int i = 1; i < NG; ++i)
+      if (i < ga.count && u >= ga.g[i].ubase) gi = i;
+  }
+  return gi;
+}
+
+// Buffer resources of one product's operands.
+struct Res {
+  __amdgpu_buffer_rsrc_t h, l, x, p, e, base, y;
+};
+__device__ __forceinline__ Res make_res(const GemmArgs& g) {
+  Res r;
+  r.h = make_rsrc(g.hi, g.hi_bytes);
+  r.l = make_rsrc(g.lo, g.lo_bytes);
+  r.x = make_rsrc(g.X, g.x_bytes);
+  r.p = make_rsrc(g.esc_ptr, (uint32_t)(g.N + 1) * 4u);
+  r.e = make_rsrc(g.esc, g.esc_bytes);
+  r.base = make_rsrc(g.base, (uint32_t)g.N);
+  r.y = make_rsrc(g.Y, g.y_bytes);
+  return r;
+}
 
 // ------------------------------------------------------------------------------------------
 // Reading the ring.  The compiler's waits for buffer-to-LDS loads model each DMA as a 16-byte
@@ -575,20 +614,23 @@ __device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict
 
 // Per-lane geometry of one segment (the stretch of one tile inside a work-group's range).
 struct SegGeo {
-  int64_t u, seg_end, tile, t0, rg;
+  int64_t u, seg_end, tile, t0, rg;   // tile: index within its product; u, seg_end, t0: launch units
   int m0;
+  int gi;                             // the product (group member) of the segment
   SegLane sl;
   uint32_t soff_h[kRB];
   uint32_t xc0[2], xc_end[2];   // chunks of the lane groups this lane fetches X for (Path::x_groups)
 };
 
 template <class Path>
-__device__ __forceinline__ void seg_setup(const GemmArgs& g, int64_t u, int64_t u_end, bool interleaved, SegGeo& s) {
+__device__ __forceinline__ void seg_setup(const GemmArgs& g, int gi, int64_t u, int64_t u_end, bool interleaved,
+                                          SegGeo& s) {
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int q = wave * 4 + (lane >> 4);
   s.u = u;
-  s.tile = u / g.upt;
-  s.t0 = s.tile * g.upt;
+  s.gi = gi;
+  s.tile = (u - g.ubase) / g.upt;
+  s.t0 = g.ubase + s.tile * g.upt;
   s.seg_end = u_end < s.t0 + g.upt ? u_end : s.t0 + g.upt;
   s.rg = s.tile / g.MT;
   s.m0 = (int)(s.tile - s.rg * g.MT);
@@ -657,9 +699,8 @@ __device__ __forceinline__ void wait_pending(int pend) {
 // kQ: the Q pass of two-level verification (news article, two-level verification part): the
 // same GEMM on the nested 8-bit view, i.e. every in-window weight with its four low mantissa
 // bits zero (the lo plane is never read: its ring slots hold zeros) and escapes exact.
-template <class Path, bool kQ>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
-void k_gemm(GemmArgs g) {
+template <class Path, bool kQ, int NG>
+__device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   constexpr int RB = kRB;
   constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
@@ -673,19 +714,22 @@ void k_gemm(GemmArgs g) {
   __shared__ float red[TILE_ELEMS];
   __shared__ uint32_t s_flag[kMaxPend];
   __shared__ uint32_t s_pend[kMaxPend];   // tiles of this work-group's partial segments
+  __shared__ uint32_t s_pendg[kMaxPend];  // and their products
   const int wave = wave_id();
+  // units, G and P are launch-wide: the same in every member of a group
+  const int64_t u_first = ubeg(ga.g[0], blockIdx.x);
+  const int64_t u_end = ubeg(ga.g[0], (int64_t)blockIdx.x + 1);
+  if (u_first >= u_end) return;
+  const int gi_first = gemm_of(ga, u_first);
+  // the first segment's product (the segment loop re-binds g and the resources per segment)
+  const GemmArgs& g = ga.g[gi_first];
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(g.lo, g.lo_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.X, g.x_bytes);
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(g.esc_ptr, (uint32_t)(g.N + 1) * 4u);
   const __amdgpu_buffer_rsrc_t re = make_rsrc(g.esc, g.esc_bytes);
   const __amdgpu_buffer_rsrc_t rbase = make_rsrc(g.base, (uint32_t)g.N);
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(g.Y, g.y_bytes);
   const __amdgpu_buffer_rsrc_t rpart = make_rsrc(g.P, g.p_bytes);
-
-  const int64_t u_first = ubeg(g, blockIdx.x);
-  const int64_t u_end = ubeg(g, (int64_t)blockIdx.x + 1);
-  if (u_first >= u_end) return;
   if constexpr (kQ) {
     // the lo slots of both ring stages read as zero nibbles (made visible by the prologue's
     // barrier, before any stage is read)
@@ -706,7 +750,7 @@ void k_gemm(GemmArgs g) {
   // ---- prologue: the first segment's escape metadata and stage 0 (interleaved mapping
   // assumed), then the escape slice ----
   SegGeo cur;
-  seg_setup<Path>(g, u_first, u_end, true, cur);
+  seg_setup<Path>(g, gi_first, u_first, u_end, true, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
   auto issue_stage0 = [&]() {
     issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
@@ -722,7 +766,7 @@ void k_gemm(GemmArgs g) {
   if ((s1 - s0) > (uint32_t)kSliceEntries) {
     // escape lists too long for LDS: contiguous mapping; stage 0 again (the first copy has landed)
     wait_vmcnt<0>();
-    seg_setup<Path>(g, u_first, u_end, false, cur);
+    seg_setup<Path>(g, gi_first, u_first, u_end, false, cur);
     issue_stage0();
   }
   issue_slice(re, s0, &slices[0][0], wave);
@@ -749,25 +793,28 @@ void k_gemm(GemmArgs g) {
     wait_vm_all();   // this work-group's partial stores are complete
     __syncthreads();
     if (threadIdx.x < (unsigned)npend) {
+      const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[threadIdx.x] : 0];
       const int64_t tile = s_pend[threadIdx.x];
-      const int64_t t0 = tile * g.upt;
-      const uint32_t nsegs = (uint32_t)(ceil_div((t0 + g.upt) * g.G, g.units) - ceil_div((t0 + 1) * g.G, g.units) + 1);
-      const uint32_t prev = __hip_atomic_fetch_add(g.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int64_t t0 = gt.ubase + tile * gt.upt;
+      const uint32_t nsegs =
+          (uint32_t)(ceil_div((t0 + gt.upt) * gt.G, gt.units) - ceil_div((t0 + 1) * gt.G, gt.units) + 1);
+      const uint32_t prev = __hip_atomic_fetch_add(gt.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
     }
     __syncthreads();
     for (int p = 0; p < npend; ++p) {
       if (!s_flag[p]) continue;
+      const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[p] : 0];
       const int64_t tile = s_pend[p];
-      const int64_t t0 = tile * g.upt;
-      const int64_t w_a = ceil_div((t0 + 1) * g.G, g.units) - 1;
-      const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
+      const int64_t t0 = gt.ubase + tile * gt.upt;
+      const int64_t w_a = ceil_div((t0 + 1) * gt.G, gt.units) - 1;
+      const int64_t w_b = ceil_div((t0 + gt.upt) * gt.G, gt.units) - 1;
       const int64_t ns = w_b - w_a + 1;
       // the tile is the first segment of every contributor except possibly w_a
-      const int pos_a = ubeg(g, w_a) < t0 ? 1 : 0;
+      const int pos_a = ubeg(gt, w_a) < t0 ? 1 : 0;
       auto slot_of = [&](int64_t j) -> int64_t { return 2 * (w_a + j) + (j == 0 ? pos_a : 0); };
-      const int64_t rg = tile / g.MT;
-      const int m0 = (int)(tile - rg * g.MT) * MROWS;
+      const int64_t rg = tile / gt.MT;
+      const int m0 = (int)(tile - rg * gt.MT) * MROWS;
       // every load of a batch (up to 64 per thread: KB <= 16 slots x ET elements) is issued
       // before any is summed; the sum still runs in work-group order
       constexpr int KB = ET >= 64 ? 1 : (64 / ET < 16 ? 64 / ET : 16);
@@ -779,7 +826,7 @@ void k_gemm(GemmArgs g) {
 #pragma unroll
         for (int sg = 0; sg < KB; ++sg) {
           if (b0 + sg < ns) {
-            const float* src = g.P + slot_of(b0 + sg) * (int64_t)TILE_ELEMS;
+            const float* src = gt.P + slot_of(b0 + sg) * (int64_t)TILE_ELEMS;
 #pragma unroll
             for (int k = 0; k < ET; ++k) {
               const int e = (int)threadIdx.x + k * kThreads;
@@ -802,10 +849,10 @@ void k_gemm(GemmArgs g) {
           const int row = e % ROWS, ml = e / ROWS;
           const int64_t n = rg * ROWS + row;
           const int m = m0 + ml;
-          if (n < g.N && m < g.M) g.Y[(int64_t)m * g.ldy + n] = v[k];
+          if (n < gt.N && m < gt.M) gt.Y[(int64_t)m * gt.ldy + n] = v[k];
         }
       }
-      if (threadIdx.x == 0) __hip_atomic_store(g.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_store(gt.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -814,10 +861,17 @@ void k_gemm(GemmArgs g) {
   // the previous segment's output stores, so no store is ever among the instructions a stage
   // wait looks past (stores and loads may complete out of order on the shared counter).
   for (;;) {
-    // the next segment: the rest of the range
+    // this segment's product and its operands (shadowing the prologue's)
+    const GemmArgs& g = ga.g[cur.gi];
+    const Res r = make_res(g);
+    const __amdgpu_buffer_rsrc_t rh = r.h, rl = r.l, rx = r.x, ry = r.y;
+    // the next segment: the rest of the range, possibly in the next product
     const int64_t nu0 = cur.seg_end, nu1 = u_end;
     const bool has_next = nu0 < nu1;
-    const int64_t nrg = has_next ? (nu0 / g.upt) / g.MT : 0;
+    const int ngi = has_next ? gemm_of(ga, nu0) : cur.gi;
+    const GemmArgs& ng = ga.g[ngi];
+    const Res nr = make_res(ng);
+    const int64_t nrg = has_next ? ((nu0 - ng.ubase) / ng.upt) / ng.MT : 0;
     SegEsc nse;
     uint32_t ns0 = 0, ns1 = 0;
     typename Path::Acc acc[RB][Path::kAcc];
@@ -859,7 +913,7 @@ void k_gemm(GemmArgs g) {
         pend = V;
       }
       if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
-        load_seg_esc(g, rp, rbase, nrg, nse);
+        load_seg_esc(ng, nr.p, nr.base, nrg, nse);
         pend += 2 * RB;
       }
       compute(ah0, al0, &xring0, xa0, xb0, j, pend);
@@ -877,8 +931,8 @@ void k_gemm(GemmArgs g) {
         pend = V;
       }
       if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
-        slice_range(g, nrg, nse, ns0, ns1);
-        issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+        slice_range(ng, nrg, nse, ns0, ns1);
+        issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
         next_sliced = true;
         pend += 1;
       }
@@ -887,8 +941,8 @@ void k_gemm(GemmArgs g) {
 
     // ---- segment end ----
     if (has_next && !next_sliced) {   // a one-step segment
-      slice_range(g, nrg, nse, ns0, ns1);
-      issue_slice(re, ns0, &slices[sb ^ 1][0], wave);
+      slice_range(ng, nrg, nse, ns0, ns1);
+      issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
     }
     wait_vmcnt<0>();   // this wave's part of the next slice has landed
     // waves add their partial tiles into red in wave order
@@ -922,33 +976,49 @@ void k_gemm(GemmArgs g) {
       }
     }
     if (!full) {
-      if (threadIdx.x == 0) s_pend[npend] = (uint32_t)cur.tile;   // read after a barrier
+      if (threadIdx.x == 0) {   // read after a barrier
+        s_pend[npend] = (uint32_t)cur.tile;
+        s_pendg[npend] = (uint32_t)cur.gi;
+      }
       ++npend;
     }
     if (!has_next) break;
     {
       SegGeo nx;
-      seg_setup<Path>(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
-      issue_w<RB, kQ>(g, rh, rl, nx.soff_h, nx.sl, 0, &ring0, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(g, rx, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
-      else Path::load_x(g, rx, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
+      seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+      issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 0, &ring0, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(ng, nr.x, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
+      else Path::load_x(ng, nr.x, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
     }
     barrier();   // red is free again; the next slice is visible to every wave
     // switch to the next segment
-    seg_setup<Path>(g, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
+    seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
     sb ^= 1;
     in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       uint32_t lo, hi;
-      seg_bounds(g, cur.rg, rb, nse, lo, hi);
+      seg_bounds(ng, cur.rg, rb, nse, lo, hi);
       bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
-      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+      esc_start(cur_esc[rb], ng, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
     }
   }
 
   // ---- deferred split-K fixups ----
   if (npend) flush_pending();
+}
+
+template <class Path, bool kQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
+void k_gemm(GroupArgs<1> ga) {
+  gemm_body<Path, kQ, 1>(ga);
+}
+
+// Up to kGroupMax independent products of the same M in one launch.
+template <class Path, bool kQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
+void k_gemm_group(GroupArgs<kGroupMax> ga) {
+  gemm_body<Path, kQ, kGroupMax>(ga);
 }
 
 __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
@@ -972,14 +1042,15 @@ __global__ __launch_bounds__(256) void k_pad_x(const uint16_t* __restrict__ X, i
 // Resident work-groups per CU of one kernel variant, from the runtime occupancy calculator
 // (registers and LDS of the compiled kernel); when no device is visible, a conservative
 // estimate.  Cached per variant.
-template <class Path, bool kQ = false>
+template <class Path, bool kGroup = false>
 static int occupancy_of(int fallback) {
   static std::once_flag once;
   static int v = 0;
   std::call_once(once, [fallback] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemm<Path, kQ>), kThreads, 0) ==
-            hipSuccess && n > 0)
+    const void* fn = kGroup ? reinterpret_cast<const void*>(&k_gemm_group<Path, false>)
+                            : reinterpret_cast<const void*>(&k_gemm<Path, false>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) == hipSuccess && n > 0)
       v = n;
     else {
       (void)hipGetLastError();
@@ -994,24 +1065,25 @@ struct GemvPath;
 template <int MB>
 struct MfmaPath;
 
+template <bool kGroup>
 static int groups_per_cu(int path, int M, int m_tile) {
   if (path == 1) {
     switch (M) {
-      case 1: return occupancy_of<GemvPath<1>>(2);
-      case 2: return occupancy_of<GemvPath<2>>(2);
-      case 3: return occupancy_of<GemvPath<3>>(2);
-      case 4: return occupancy_of<GemvPath<4>>(2);
-      case 5: return occupancy_of<GemvPath<5>>(2);
-      case 6: return occupancy_of<GemvPath<6>>(2);
-      case 7: return occupancy_of<GemvPath<7>>(2);
-      default: return occupancy_of<GemvPath<8>>(2);
+      case 1: return occupancy_of<GemvPath<1>, kGroup>(2);
+      case 2: return occupancy_of<GemvPath<2>, kGroup>(2);
+      case 3: return occupancy_of<GemvPath<3>, kGroup>(2);
+      case 4: return occupancy_of<GemvPath<4>, kGroup>(2);
+      case 5: return occupancy_of<GemvPath<5>, kGroup>(2);
+      case 6: return occupancy_of<GemvPath<6>, kGroup>(2);
+      case 7: return occupancy_of<GemvPath<7>, kGroup>(2);
+      default: return occupancy_of<GemvPath<8>, kGroup>(2);
     }
   }
   switch (m_tile / 16) {
-    case 1: return occupancy_of<MfmaPath<1>>(2);
-    case 2: return occupancy_of<MfmaPath<2>>(2);
-    case 3: return occupancy_of<MfmaPath<3>>(1);
-    default: return occupancy_of<MfmaPath<4>>(1);
+    case 1: return occupancy_of<MfmaPath<1>, kGroup>(2);
+    case 2: return occupancy_of<MfmaPath<2>, kGroup>(2);
+    case 3: return occupancy_of<MfmaPath<3>, kGroup>(1);
+    default: return occupancy_of<MfmaPath<4>, kGroup>(1);
   }
 }
 
@@ -1050,7 +1122,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   p.tiles = p.row_groups * p.m_tiles;
   p.upt = (Kc + kUnitChunks - 1) / kUnitChunks;
   p.units = p.tiles * p.upt;
-  const int gpc = p.path == 3 ? wide_groups_per_cu(p.m_tile) : groups_per_cu(p.path, M, p.m_tile);
+  const int gpc = p.path == 3 ? wide_groups_per_cu(p.m_tile) : groups_per_cu<false>(p.path, M, p.m_tile);
   int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", gpc);
   const int max_grid = env_int("W12_MAX_GRID", 0);   // 0: no cap
   if (max_grid > 0 && G > max_grid) G = max_grid;
@@ -1087,15 +1159,21 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   return p;
 }
 
-template <class Path>
-static void launch_path(const GemmPlan& p, const GemmArgs& a, bool qpass, hipStream_t stream) {
-  if (qpass) hipLaunchKernelGGL((k_gemm<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
-  else hipLaunchKernelGGL((k_gemm<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+template <class Path, int NG>
+static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, hipStream_t stream) {
+  if constexpr (NG == 1) {
+    if (qpass) hipLaunchKernelGGL((k_gemm<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_gemm<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+  } else {
+    if (qpass) hipLaunchKernelGGL((k_gemm_group<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_gemm_group<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+  }
 }
 
-static void dispatch(const GemmPlan& p, const GemmArgs& a, bool qpass, hipStream_t stream) {
+template <int NG>
+static void dispatch(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, hipStream_t stream) {
   if (p.path == 1) {
-    switch (a.M) {
+    switch (a.g[0].M) {
       case 1: launch_path<GemvPath<1>>(p, a, qpass, stream); break;
       case 2: launch_path<GemvPath<2>>(p, a, qpass, stream); break;
       case 3: launch_path<GemvPath<3>>(p, a, qpass, stream); break;
@@ -1123,6 +1201,9 @@ hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
+static void fill_args(GemmArgs& a, const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t,
+                      float* Y, int64_t ldy, void* ws);
+
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream) {
   GemmArgs a;
@@ -1137,6 +1218,24 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
     ldx = kp;
   }
   if (p.path == 3) return launch_gemm_wide(p, X, M, ldx, t, Y, ldy, ws, qpass, stream);
+  fill_args(a, p, X, M, ldx, t, Y, ldy, ws);
+  a.ubase = 0;
+  a.tiles = p.tiles;
+  a.upt = p.upt;
+  a.units = p.units;
+  a.counters = reinterpret_cast<uint32_t*>(ws);
+  GroupArgs<1> ga;
+  ga.g[0] = a;
+  ga.count = 1;
+  dispatch(p, ga, qpass, stream);
+  return hipGetLastError();
+}
+
+// The operand fields of one product (everything but its place in the launch's unit space and
+// its counters).
+static void fill_args(GemmArgs& a, const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t,
+                      float* Y, int64_t ldy, void* ws) {
+  a.Kc = num_chunks(t->K);
   a.X = X;
   a.ldx = ldx;
   a.base = t->base;
@@ -1150,9 +1249,6 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   a.K = t->K;
   a.Nb = num_row_blocks(t->N);
   a.MT = p.m_tiles;
-  a.tiles = p.tiles;
-  a.upt = p.upt;
-  a.units = p.units;
   a.G = p.grid;
   const uint64_t chunks = (uint64_t)a.Nb * (uint64_t)a.Kc;
   a.hi_bytes = (uint32_t)(chunks * kHiChunkBytes);
@@ -1162,10 +1258,94 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   a.Y = Y;
   a.ldy = ldy;
   a.y_bytes = (uint32_t)((((uint64_t)M - 1) * (uint64_t)ldy + (uint64_t)t->N) * 4u);
-  a.counters = reinterpret_cast<uint32_t*>(ws);
   a.P = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes);
   a.p_bytes = (uint32_t)p.partial_bytes;
-  dispatch(p, a, qpass, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// Grouped launch: up to kGroupMax independent products with the same M (and K % 16 == 0,
+// M <= 64: the streaming tiles) in one stream-K launch over their concatenated unit spaces.
+// Launch gaps, the pipeline fill at the start and the split-K fixups at the end are paid once
+// per launch instead of once per product.
+// ------------------------------------------------------------------------------------------
+GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32_t* K, int64_t* tiles_of,
+                         int64_t* upt_of) {
+  GemmPlan p{};
+  int gemv_max = env_int("W12_GEMV_MAX_M", kGemvMaxM);
+  gemv_max = gemv_max < 0 ? 0 : (gemv_max > 8 ? 8 : gemv_max);
+  p.path = M <= gemv_max ? 1 : 2;
+  p.rb = kRB;
+  p.waves = kWaves;
+  if (p.path == 1) {
+    p.m_tile = M;
+    p.m_tiles = 1;
+  } else {
+    const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 48 ? 3 : 4));
+    p.m_tile = 16 * mb;
+    p.m_tiles = (M + p.m_tile - 1) / p.m_tile;
+  }
+  p.tiles = 0;
+  p.units = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t rg = (num_row_blocks(N[i]) + p.rb - 1) / p.rb;
+    tiles_of[i] = rg * p.m_tiles;
+    upt_of[i] = (num_chunks(K[i]) + kUnitChunks - 1) / kUnitChunks;
+    p.tiles += tiles_of[i];
+    p.units += tiles_of[i] * upt_of[i];
+  }
+  p.row_groups = 0;
+  p.upt = 0;   // per product (upt_of)
+  int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", groups_per_cu<true>(p.path, M, p.m_tile));
+  const int max_grid = env_int("W12_MAX_GRID", 0);
+  if (max_grid > 0 && G > max_grid) G = max_grid;
+  if (G > p.units) G = p.units;
+  if (G < 1) G = 1;
+  p.grid = G;
+  // most segments meeting one tile
+  {
+    int64_t best = 1, run_tile = -1, run = 0;
+    for (int64_t w = 1; w < G; ++w) {
+      int64_t u = w * p.units / G, gt = 0;
+      int i = 0;
+      while (u >= tiles_of[i] * upt_of[i]) {
+        u -= tiles_of[i] * upt_of[i];
+        gt += tiles_of[i];
+        ++i;
+      }
+      if (u % upt_of[i] == 0) continue;
+      const int64_t t = gt + u / upt_of[i];
+      run = (t == run_tile) ? run + 1 : 1;
+      run_tile = t;
+      best = run + 1 > best ? run + 1 : best;
+    }
+    p.splits = (int)best;
+  }
+  const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
+  p.counter_bytes = ((uint64_t)p.tiles * 4 + 255) / 256 * 256;
+  p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
+  p.xpad_bytes = 0;
+  p.ws_bytes = p.counter_bytes + p.partial_bytes;
+  return p;
+}
+
+hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const w12_gemm_item* items,
+                             const int64_t* tiles_of, const int64_t* upt_of, void* ws, bool qpass, hipStream_t stream) {
+  GroupArgs<kGroupMax> ga{};
+  int64_t ubase = 0, tbase = 0;
+  for (int i = 0; i < count; ++i) {
+    GemmArgs& a = ga.g[i];
+    fill_args(a, p, items[i].X, M, items[i].ldx, items[i].t, items[i].Y, items[i].ldy, ws);
+    a.ubase = ubase;
+    a.tiles = tiles_of[i];
+    a.upt = upt_of[i];
+    a.units = p.units;
+    a.counters = reinterpret_cast<uint32_t*>(ws) + tbase;
+    ubase += tiles_of[i] * upt_of[i];
+    tbase += tiles_of[i];
+  }
+  for (int i = count; i < kGroupMax; ++i) ga.g[i] = ga.g[0];   // never selected (count bounds gemm_of)
+  ga.count = count;
+  dispatch(p, ga, qpass, stream);
   return hipGetLastError();
 }
 

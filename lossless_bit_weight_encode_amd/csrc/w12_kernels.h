@@ -46,6 +46,13 @@ hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int
                             float* Y, int64_t ldy, void* ws, bool qpass, hipStream_t stream);
 
 hipError_t init_gemm_workspace(void* ws, uint64_t bytes, hipStream_t stream);
+// Grouped launch (several independent products of the same M, M <= 64, K % 16 == 0):
+// tiles_of / upt_of receive each product's tile count and units per tile.
+GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32_t* K, int64_t* tiles_of,
+                         int64_t* upt_of);
+hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const w12_gemm_item* items,
+                             const int64_t* tiles_of, const int64_t* upt_of, void* ws, bool qpass,
+                             hipStream_t stream);
 // qpass: the Q pass on the nested 8-bit view (hi plane only, escapes exact)
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream);

@@ -170,3 +170,61 @@ def test_gemm_grid_cap_env(monkeypatch, cap):
         p = w12.gemm_plan(m, n, k)
         assert 1 <= p["grid"] <= cap
         assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]
+
+
+def _items(descs, m, x=0x10000, y=0x20000):
+    items = (L._GemmItem * len(descs))()
+    for i, d in enumerate(descs):
+        items[i].X, items[i].ldx = x, d.K
+        items[i].t = ctypes.pointer(d)
+        items[i].Y, items[i].ldy = y, d.N
+    return items
+
+
+def test_gemm_group_argument_validation():
+    lib = w12.lib()
+    d = [_desc(n=5120, k=5120), _desc(n=5120, k=17408)]
+    items = _items(d, 16)
+    need = L._c_u64()
+    assert lib.w12_gemm_group_workspace_size(16, 2, items, ctypes.byref(need)) == 0
+    assert need.value > 0
+    assert lib.w12_gemm_group_workspace_size(16, 0, items, ctypes.byref(need)) == -2
+    assert lib.w12_gemm_group_workspace_size(16, L.GROUP_MAX + 1, items, ctypes.byref(need)) == -2
+    assert lib.w12_gemm_group_workspace_size(65, 2, items, ctypes.byref(need)) == -2
+    assert lib.w12_gemm_group_workspace_size(0, 2, items, ctypes.byref(need)) == -2
+    assert lib.w12_gemm_group_workspace_size(16, 2, None, ctypes.byref(need)) == -1
+    # K not a multiple of 16
+    bad = _items([_desc(n=64, k=1000)], 4)
+    assert lib.w12_gemm_group_workspace_size(4, 1, bad, ctypes.byref(need)) == -2
+    # a bad member descriptor names its item
+    bad = _items([_desc(n=64, k=1024), _desc(n=64, k=1024, hi=0)], 4)
+    assert lib.w12_gemm_group_workspace_size(4, 2, bad, ctypes.byref(need)) == -1
+    assert "item 1" in lib.w12_last_error().decode()
+    # operand checks, workspace size
+    lib.w12_gemm_group_workspace_size(16, 2, items, ctypes.byref(need))
+    assert lib.w12_gemm_group(16, 2, items, 0x100000, need.value - 1, None) == -3
+    assert lib.w12_gemm_group(16, 2, items, None, need.value, None) == -1
+    assert lib.w12_gemm_group(16, 2, items, 0x100008, need.value, None) == -5
+    items[1].X = 0x10002
+    assert lib.w12_gemm_group(16, 2, items, 0x100000, need.value, None) == -5
+    assert "item 1" in lib.w12_last_error().decode()
+    items[1].X = 0x10000
+    items[0].Y = None
+    assert lib.w12_gemm_group_q(16, 2, items, 0x100000, need.value, None) == -1
+    items[0].Y = 0x20000
+    items[0].ldy = 10
+    assert lib.w12_gemm_group(16, 2, items, 0x100000, need.value, None) == -1
+
+
+@pytest.mark.parametrize("m", [1, 16, 32, 64])
+def test_gemm_group_workspace_covers_counters_and_partials(m):
+    """The group workspace holds one counter per tile of every product and two partial tiles per
+    work-group; a group of one needs no more than the single launch's counters and partials."""
+    d = [_desc(n=7168, k=5120), _desc(n=5120, k=5120), _desc(n=34816, k=5120), _desc(n=5120, k=17408)]
+    need = L._c_u64()
+    assert w12.lib().w12_gemm_group_workspace_size(m, 4, _items(d, m), ctypes.byref(need)) == 0
+    tiles = sum(-(-(-(-dd.N // 16)) // 4) for dd in d)
+    assert need.value >= 4 * tiles
+    one = L._c_u64()
+    assert w12.lib().w12_gemm_group_workspace_size(m, 1, _items(d[2:3], m), ctypes.byref(one)) == 0
+    assert one.value <= need.value

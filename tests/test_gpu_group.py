@@ -1,0 +1,155 @@
+"""GPU parity of the grouped launch (w12_gemm_group / w12_gemm_group_q): several independent
+W12 products of one M in one stream-K launch.
+
+Every product's Y is checked against the FP64 oracle within 2^-12 * sum|x w| (the exact pass
+against W, the Q pass against the oracle's Q view), bitwise repeatable, and compared with the
+single-product launch.  Small work-group counts force work-group ranges that cross product
+boundaries and tiles split over many work-groups.  The full decoder-layer group is checked on
+sampled channels at the sizes and launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lossless_bit_weight_encode_amd as w12
+import w12_synth as S
+from oracle import w12_oracle as O
+from gpu_util import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# mixed shapes, every K a multiple of 16: tiny case with infs, a 40-binade mix, heavy tails,
+# a channel of zeros only, a single row block, a ragged N
+MEMBERS = {
+    "tiny_256x512": lambda: S.tiny_weights(0),
+    "gauss_300x4096": lambda: S.layer_matrix(torch.Generator().manual_seed(5), 300, 4096),
+    "heavy_64x2048": lambda: S.heavy_tail_weights(1000, 64, 2048),
+    "wide_37x1008": lambda: S.random_bits_matrix(np.random.default_rng(11), 37, 1008, "wide"),
+    "all_escapes_20x96": lambda: np.zeros((20, 96), dtype=np.uint16),
+    "single_1x16": lambda: S.random_bits_matrix(np.random.default_rng(4), 1, 16, "wide"),
+    "gauss_130x640": lambda: S.layer_matrix(torch.Generator().manual_seed(6), 130, 640),
+    "wide_70x272": lambda: S.random_bits_matrix(np.random.default_rng(12), 70, 272, "wide"),
+}
+_cache = {}
+
+
+def member(name):
+    if name not in _cache:
+        w = MEMBERS[name]()
+        _cache[name] = (w, w12.encode(to_dev(w)), O.encode(w))
+    return _cache[name]
+
+
+def run_group(names, m, seed, qpass=False, repeats=2):
+    ws_, ts, xs = [], [], []
+    for i, nm in enumerate(names):
+        w, t, _ = member(nm)
+        ws_.append(w)
+        ts.append(t)
+        xs.append(S.activations(m, w.shape[1], 7000 + seed + 31 * i + m))
+    xd = [to_dev(x) for x in xs]
+    ws = w12.gemm_group_workspace(m, ts)
+    ys = w12.gemm_group(xd, ts, ws=ws, qpass=qpass)
+    torch.cuda.synchronize()
+    for _ in range(repeats - 1):
+        ys2 = w12.gemm_group(xd, ts, ws=ws, qpass=qpass)
+        torch.cuda.synchronize()
+        for a, b in zip(ys, ys2):
+            assert torch.equal(a, b), "grouped GEMM output is not bitwise repeatable"
+    # every call leaves the arrival counters (one per 64-channel tile, at the start) zero
+    tiles = sum(-(-(-(-t.n // 16)) // 4) for t in ts)
+    assert int(ws[:4 * tiles].count_nonzero()) == 0
+    for i, nm in enumerate(names):
+        yh = ys[i].cpu().numpy()
+        if qpass:
+            bad, worst = O.gemm_q_check(xs[i], member(nm)[2], yh)
+        else:
+            bad, worst = O.gemm_check(xs[i], ws_[i], yh)
+        assert bad == 0, f"{nm} (item {i}) M={m}: {bad} outputs outside tolerance (worst rel {worst:.3g})"
+    return xs, xd, ys
+
+
+ALL = list(MEMBERS)
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 8, 16, 17, 32, 33, 48, 64])
+def test_group_within_tolerance(m):
+    say(f"[group] M={m} members={len(ALL)}")
+    run_group(ALL, m, seed=0)
+
+
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 50])
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_group_small_grids(monkeypatch, grid, m):
+    """Few work-groups: ranges cross product boundaries and tiles split over many segments."""
+    monkeypatch.setenv("W12_MAX_GRID", str(grid))
+    run_group(ALL[:5], m, seed=100 + grid)
+
+
+@pytest.mark.parametrize("m", [3, 5, 8])
+def test_group_gemv_path(monkeypatch, m):
+    monkeypatch.setenv("W12_GEMV_MAX_M", "8")
+    run_group(ALL, m, seed=200)
+
+
+@pytest.mark.parametrize("m", [1, 16, 33, 64])
+def test_group_qpass_within_tolerance(m):
+    run_group(ALL, m, seed=300, qpass=True)
+
+
+def test_group_sizes_one_to_max():
+    for count in range(1, w12.GROUP_MAX + 1):
+        names = [ALL[(3 * i) % len(ALL)] for i in range(count)]
+        run_group(names, 16, seed=400 + count, repeats=1)
+
+
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_group_matches_single_launch(m):
+    """Grouped and single launches agree up to the FP32 summation order (each is within 2^-12 of
+    the exact sum, so they differ by at most 2^-11 * sum|x w|)."""
+    xs, xd, ys = run_group(ALL, m, seed=500, repeats=1)
+    for i, nm in enumerate(ALL):
+        w, t, _ = member(nm)
+        y1 = w12.gemm(xd[i], t).cpu().numpy().astype(np.float64)
+        _, a_ref = O.gemm_reference(xs[i], w)
+        fin = np.isfinite(y1)
+        assert (np.abs(y1[fin] - ys[i].cpu().numpy()[fin]) <= 2.0 ** -11 * a_ref[fin]).all(), nm
+
+
+def test_group_rejects_unsupported():
+    w, t, _ = member("gauss_300x4096")
+    x = to_dev(S.activations(65, w.shape[1], 1))
+    with pytest.raises(w12.W12Error):
+        w12.gemm_group([x], [t])
+    wr = S.random_bits_matrix(np.random.default_rng(3), 17, 33, "wide")
+    tr = w12.encode(to_dev(wr, 40))
+    with pytest.raises(w12.W12Error):
+        w12.gemm_group([to_dev(S.activations(4, 33, 1), 40)], [tr])
+
+
+# ---- full size: one dense decoder layer in one launch, sampled channels ---------------------
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("m", [1, 16, 32, 64])
+def test_group_layer_full_size(m):
+    say(f"[group] layer seed 0, M={m}")
+    lay = S.layer(0)
+    names = list(S.LAYER_ORDER)
+    ts = [w12.encode(to_dev(lay[nm])) for nm in names]
+    xs = [S.activations(m, S.LAYER_SHAPES[nm][1], S.x_seed(m, S.LAYER_SHAPES[nm][1])) for nm in names]
+    xd = [to_dev(x) for x in xs]
+    ws = w12.gemm_group_workspace(m, ts)
+    ys = w12.gemm_group(xd, ts, ws=ws)
+    torch.cuda.synchronize()
+    ys2 = w12.gemm_group(xd, ts, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(m)
+    for i, nm in enumerate(names):
+        assert torch.equal(ys[i], ys2[i]), f"{nm}: not bitwise repeatable"
+        n = S.LAYER_SHAPES[nm][0]
+        rows = np.array(sorted(set(range(64)) | set(range(n - 64, n)) |
+                               set(rng.choice(n, 128, replace=False).tolist())))
+        yh = ys[i].cpu().numpy()
+        bad, worst = O.gemm_check(xs[i], lay[nm][rows], yh[:, rows])
+        assert bad == 0, f"{nm} M={m}: {bad} sampled outputs outside tolerance (worst rel {worst:.3g})"
+        assert np.isfinite(yh).all()
