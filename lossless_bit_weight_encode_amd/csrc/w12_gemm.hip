@@ -705,6 +705,8 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
   constexpr int V = Path::kVmemPerStage - (kQ ? 2 : 0);   // the Q pass issues no lo loads
+  // loads of a stage 0 issued before a segment's epilogue (register X follows the stores)
+  constexpr int V0 = Path::kXInLds ? V : V - 2 * Path::kAcc;
   constexpr int TILE_ELEMS = ROWS * MROWS;
   constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;   // output elements per thread
   typedef typename Path::XStage XStage;
@@ -944,7 +946,21 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       slice_range(ng, nrg, nse, ns0, ns1);
       issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
     }
-    wait_vmcnt<0>();   // this wave's part of the next slice has landed
+    // The next segment's stage 0 goes out now, so its latency overlaps the reduction and the
+    // output stores below: every ring slot of this wave has been read (each stage's LDS reads
+    // are waited for in the statement that issues them).  Register X (two 16-row blocks) is
+    // loaded after the stores instead: the compiler waits for those registers itself, and its
+    // count would include the stores.  Later stage waits count loads only, and loads complete
+    // in issue order, so the stores in between can only make a wait longer.
+    SegGeo nx;
+    if (has_next) {
+      seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+      issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 0, &ring0, wave);
+      if constexpr (Path::kXInLds) Path::issue_x(ng, nr.x, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
+      wait_vmcnt<V0>();   // this wave's part of the next slice has landed (it precedes stage 0)
+    } else {
+      wait_vmcnt<0>();
+    }
     // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
       if (wave == w) Path::to_red(acc, red_addr, w == 0);
@@ -976,23 +992,21 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       }
     }
     if (!full) {
-      if (threadIdx.x == 0) {   // read after a barrier
-        s_pend[npend] = (uint32_t)cur.tile;
-        s_pendg[npend] = (uint32_t)cur.gi;
+      // read after a barrier; written with explicit LDS stores, which the compiler does not
+      // order behind the stage-0 DMA still in flight
+      if (threadIdx.x == 0) {
+        lds_write_u32(lds_off(&s_pend[0]) + 4u * (uint32_t)npend, (uint32_t)cur.tile);
+        lds_write_u32(lds_off(&s_pendg[0]) + 4u * (uint32_t)npend, (uint32_t)cur.gi);
+        wait_lgkm();
       }
       ++npend;
     }
     if (!has_next) break;
-    {
-      SegGeo nx;
-      seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
-      issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 0, &ring0, wave);
-      if constexpr (Path::kXInLds) Path::issue_x(ng, nr.x, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
-      else Path::load_x(ng, nr.x, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
-    }
+    if constexpr (!Path::kXInLds) Path::load_x(ng, nr.x, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
+    wait_lgkm();
     barrier();   // red is free again; the next slice is visible to every wave
     // switch to the next segment
-    seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, cur);
+    cur = nx;
     sb ^= 1;
     in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
 #pragma unroll
