@@ -154,6 +154,8 @@ def main():
         }
         log(f"[bench] {nm}: E={enc[nm].num_escapes} bpw={enc[nm].bits_per_weight():.4f} "
             f"encode {t_enc:.3f} ms verify {t_ver:.3f} ms")
+    # ---- checkpoint leg: the layer's W12 file streamed back, checked against the BF16 source ----
+    out_ckpt = checkpoint_leg(enc, w_dev, names)
     del w_dev
     torch.cuda.empty_cache()
 
@@ -244,6 +246,7 @@ def main():
     }
     out["roofline"].update(traffic_from_profile(ab))
     out["load_time"] = load_leg
+    out["checkpoint"] = out_ckpt
 
     # ---- the same four products in one grouped launch (w12_gemm_group) ----
     xs_g = [x_dev[(nm, m_step)] for nm in names]
@@ -439,6 +442,43 @@ def summarize_mfma(pmc_csv, probe_json):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def checkpoint_leg(enc, w_dev, names, reps=3):
+    """One layer's W12 checkpoint (w12_file_write), streamed back with w12_file_load through a
+    64 MiB pinned staging buffer, with and without the load-time check of each matrix against its
+    BF16 source enqueued during the load.  The file was just written, so it is read from the page
+    cache: this is the host-to-HBM path, not a disk."""
+    import tempfile
+    d = tempfile.mkdtemp(prefix="w12ckpt_")
+    path = os.path.join(d, "layer0.w12")
+    t0 = time.perf_counter()
+    w12.save(path, {nm: enc[nm] for nm in names})
+    t_save = time.perf_counter() - t0
+    file_bytes = os.path.getsize(path)
+    staging = torch.empty(64 << 20, dtype=torch.uint8, pin_memory=True)
+    res = {}
+    for label, refs in (("load_only", None), ("load_and_check", {nm: w_dev[nm] for nm in names})):
+        times = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            got, chk = w12.load(path, refs=refs, staging=staging)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            if refs:
+                assert chk[:, 0].sum().item() == 0, "checkpoint load-time check failed"
+            del got
+        t = float(np.median(times))
+        res[label] = {"s": round(t, 4), "file_GBps": round(file_bytes / t / 1e9, 2)}
+    os.remove(path)
+    os.rmdir(d)
+    log(f"[bench] checkpoint {file_bytes / 1e6:.0f} MB: load {res['load_only']['file_GBps']} GB/s, "
+        f"load + check {res['load_and_check']['file_GBps']} GB/s")
+    return {"what": "one layer's W12 file (w12_file_write) streamed to HBM with w12_file_load through 64 MiB of "
+                    "pinned staging; the check compares each matrix with its BF16 source during the load; "
+                    "the file is read from the page cache", "file_bytes": file_bytes,
+            "save_s": round(t_save, 3), **res}
 
 
 def full_model_leg(dev, stream, n_layers, m, reps=5):

@@ -58,6 +58,7 @@ extern "C" {
 #define W12_ERR_WORKSPACE_TOO_SMALL (-3)  /* ws_bytes below w12_gemm_workspace_size          */
 #define W12_ERR_HIP (-4)                  /* a HIP runtime call or kernel launch failed      */
 #define W12_ERR_MISALIGNED (-5)           /* a vector-accessed pointer or pitch is unaligned */
+#define W12_ERR_IO (-6)                   /* a checkpoint file could not be read or written  */
 
 #define W12_LAYOUT_RB16_K16 1
 
@@ -210,6 +211,49 @@ typedef struct w12_gemm_plan_info {
   uint64_t counter_bytes;    /* leading bytes of the workspace holding arrival counters */
 } w12_gemm_plan_info;
 int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info *info);
+
+/*
+ * W12 checkpoint files (summary page, result bullet of section 4.1: converted layers are
+ * checked bit for bit when they are loaded).  A file holds named encoded tensors in the
+ * physical layout above: a 64-byte header (magic "W12CKPT1", version 1, tensor count), one
+ * 128-byte index entry per tensor, then per tensor its base, esc_ptr, esc, hi and lo arrays,
+ * each starting on a 256-byte boundary.  Integers are little-endian.
+ */
+typedef struct w12_file_entry {
+  char name[64];         /* NUL-terminated (at most 63 characters are stored)           */
+  int32_t N, K;
+  int32_t layout;        /* W12_LAYOUT_RB16_K16                                          */
+  int32_t reserved;
+  int64_t num_escapes;
+  uint64_t offset;       /* file offset of the tensor's data                             */
+  uint64_t bytes;        /* bytes of the tensor's data (sections and their padding)      */
+} w12_file_entry;
+
+/* Write count tensors to path (created or truncated).  Every array of host_tensors[i] is HOST
+ * memory (copy the planes back from the device first); names[i] are C strings.  Synchronous;
+ * W12_ERR_IO on a failed open or write. */
+int w12_file_write(const char *path, int32_t count, const char *const *names, const w12_tensor *host_tensors);
+
+/* Read the index of path: *count receives the number of tensors; when entries is not NULL the
+ * first *count entries are written (W12_ERR_INVALID_ARG if *count > max_entries).  Synchronous. */
+int w12_file_index(const char *path, int32_t *count, w12_file_entry *entries, int32_t max_entries);
+
+/*
+ * Streamed load.  For i < count, copies tensor which[i] of the file into the device arrays of
+ * dst[i] (N, K, layout and num_escapes must equal the index entry; the caller sizes the arrays
+ * from the entry).  The file is read on the calling thread in pieces of staging_bytes / 2
+ * into alternating halves of `staging` (pinned host memory of at least 512 bytes), each piece
+ * copied to the device on `stream`; a half is refilled only after its previous copy has
+ * completed.  When refs is not NULL and refs[i] is not NULL, the load-time check of dst[i]
+ * against the BF16 matrix refs[i] (device, row pitch ldr[i]) is enqueued on `stream` right
+ * after the tensor's copies, with w12_verify's semantics, into d_results[2i], d_results[2i+1]
+ * (device; 2*count values).  The call returns once every copy has been enqueued and the
+ * staging buffer is no longer read; the checks may still be running.  Creates and destroys
+ * two HIP events; allocates no memory.  W12_ERR_IO on a read failure or a malformed file.
+ */
+int w12_file_load(const char *path, int32_t count, const int32_t *which, const w12_tensor *dst,
+                  void *staging, uint64_t staging_bytes, const uint16_t *const *refs, const int64_t *ldr,
+                  unsigned long long *d_results, hipStream_t stream);
 
 /* Stored bits per weight: (1.5*N*K + N + 4*(N+1) + 4*E) * 8 / (N*K). */
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E);

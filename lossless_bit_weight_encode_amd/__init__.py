@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     encode,
     encode_count,
     encode_emit,
+    file_index,
     GROUP_MAX,
     gemm,
     gemm_group,
@@ -25,6 +26,8 @@ from ._lib import (  # noqa: F401
     gemm_workspace_size,
     layout_bytes,
     lib,
+    load,
+    save,
     unpack_records,
     verify,
     verify_async,

@@ -36,6 +36,11 @@ class _GemmItem(ctypes.Structure):
 GROUP_MAX = 8
 
 
+class _FileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("N", _c_i32), ("K", _c_i32), ("layout", _c_i32), ("reserved", _c_i32),
+                ("num_escapes", _c_i64), ("offset", _c_u64), ("bytes", _c_u64)]
+
+
 class _PlanInfo(ctypes.Structure):
     _fields_ = [
         ("path", _c_i32), ("splits", _c_i32), ("rows_per_block", _c_i32), ("m_tile", _c_i32),
@@ -58,6 +63,10 @@ _SIGNATURES = {
     "w12_gemm_group_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), ctypes.POINTER(_c_u64)]),
     "w12_gemm_group": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), _c_p, _c_u64, _c_p]),
     "w12_gemm_group_q": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), _c_p, _c_u64, _c_p]),
+    "w12_file_write": (ctypes.c_int, [ctypes.c_char_p, _c_i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_Tensor)]),
+    "w12_file_index": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_c_i32), ctypes.POINTER(_FileEntry), _c_i32]),
+    "w12_file_load": (ctypes.c_int, [ctypes.c_char_p, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_Tensor), _c_p,
+                                     _c_u64, ctypes.POINTER(_c_p), ctypes.POINTER(_c_i64), _c_p, _c_p]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
     "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w12_last_error": (ctypes.c_char_p, []),
@@ -343,3 +352,75 @@ def gemm_group(xs, ts, ys=None, ws: torch.Tensor | None = None, stream=None, qpa
     name = "w12_gemm_group_q" if qpass else "w12_gemm_group"
     _check(name, getattr(lib(), name)(m, len(ts), items, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return ys
+
+
+def _host_descriptor(n, k, e, base, hi, lo, esc_ptr, esc) -> _Tensor:
+    d = _Tensor()
+    d.N, d.K, d.layout, d.reserved, d.num_escapes = n, k, W12_LAYOUT_RB16_K16, 0, e
+    d.base, d.hi, d.lo, d.esc_ptr = (a.ctypes.data for a in (base, hi, lo, esc_ptr))
+    d.esc = esc.ctypes.data if e else None
+    return d
+
+
+def save(path: str, tensors: dict) -> None:
+    """Write {name: W12Tensor} to a W12 checkpoint file (w12_file_write); the planes are copied
+    to host memory first."""
+    import numpy as np
+    names = list(tensors)
+    keep, descs = [], (_Tensor * len(names))()
+    for i, nm in enumerate(names):
+        t = tensors[nm]
+        arrs = [x.cpu().contiguous().numpy() for x in (t.base, t.hi, t.lo, t.esc_ptr, t.esc)]
+        arrs = [np.ascontiguousarray(a) for a in arrs]
+        keep.append(arrs)
+        descs[i] = _host_descriptor(t.n, t.k, t.num_escapes, arrs[0], arrs[1], arrs[2], arrs[3], arrs[4])
+    cnames = (ctypes.c_char_p * len(names))(*[nm.encode() for nm in names])
+    _check("w12_file_write", lib().w12_file_write(path.encode(), len(names), cnames, descs))
+
+
+def file_index(path: str) -> list[dict]:
+    """The index of a W12 checkpoint file (w12_file_index)."""
+    n = _c_i32()
+    _check("w12_file_index", lib().w12_file_index(path.encode(), ctypes.byref(n), None, 0))
+    entries = (_FileEntry * max(n.value, 1))()
+    _check("w12_file_index", lib().w12_file_index(path.encode(), ctypes.byref(n), entries, n.value))
+    return [{"name": e.name.decode(), "n": e.N, "k": e.K, "num_escapes": e.num_escapes, "offset": e.offset,
+             "bytes": e.bytes} for e in entries[:n.value]]
+
+
+def load(path: str, refs: dict | None = None, device="cuda", staging: torch.Tensor | None = None,
+         staging_bytes: int = 64 << 20, stream=None):
+    """Stream every tensor of a W12 checkpoint file to the GPU (w12_file_load).  With refs
+    ({name: BF16 [N, K] on the GPU}), the load-time bit-for-bit check of each named tensor is
+    enqueued right after its copies.  Returns ({name: W12Tensor}, results) where results is an
+    int64 [count, 2] device tensor of (mismatch count, first bad flat index) per tensor (zeros
+    for tensors without a reference)."""
+    idx = file_index(path)
+    if staging is None:
+        staging = torch.empty(staging_bytes, dtype=torch.uint8, pin_memory=True)
+    out, descs = {}, (_Tensor * len(idx))()
+    for i, e in enumerate(idx):
+        base, hi, lo, esc_ptr = alloc_planes(e["n"], e["k"], device)
+        esc = torch.empty(e["num_escapes"], dtype=torch.int32, device=device)
+        t = W12Tensor(e["n"], e["k"], base, hi, lo, esc_ptr, esc)
+        out[e["name"]] = t
+        descs[i] = t.descriptor()
+    which = (_c_i32 * len(idx))(*range(len(idx)))
+    results = torch.zeros(len(idx), 2, dtype=torch.int64, device=device)
+    refs_arr = ldr_arr = None
+    keep = []
+    if refs:
+        refs_arr = (_c_p * len(idx))()
+        ldr_arr = (_c_i64 * len(idx))()
+        for i, e in enumerate(idx):
+            r = refs.get(e["name"])
+            if r is not None:
+                _require_cuda(r)
+                _bits16(r)
+                keep.append(r)
+                refs_arr[i] = r.data_ptr()
+                ldr_arr[i] = _pitch(r)
+    _check("w12_file_load", lib().w12_file_load(path.encode(), len(idx), which, descs, staging.data_ptr(),
+                                                staging.numel(), refs_arr, ldr_arr, results.data_ptr(),
+                                                _stream(stream)))
+    return out, results

@@ -3,6 +3,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <vector>
+
 #include "w12_device.h"
 #include "w12_kernels.h"
 
@@ -263,6 +265,64 @@ int w12_gemm_group_q(int32_t M, int32_t count, const w12_gemm_item* items, void*
   return gemm_group_call(M, count, items, ws, ws_bytes, true, stream);
 }
 
+int w12_file_write(const char* path, int32_t count, const char* const* names, const w12_tensor* host_tensors) {
+  if (!path || !names || !host_tensors) return fail(W12_ERR_INVALID_ARG, "path, names or host_tensors is NULL");
+  if (count < 1) return fail(W12_ERR_INVALID_ARG, "count=%d must be at least 1", count);
+  for (int i = 0; i < count; ++i) {
+    if (!names[i]) return fail(W12_ERR_INVALID_ARG, "names[%d] is NULL", i);
+    int rc = check_tensor(&host_tensors[i]);
+    if (rc) return item_fail(rc, i);
+  }
+  char err[256];
+  if (w12::file_write(path, count, names, host_tensors, err, sizeof(err))) return fail(W12_ERR_IO, "%s", err);
+  return ok();
+}
+
+int w12_file_index(const char* path, int32_t* count, w12_file_entry* entries, int32_t max_entries) {
+  if (!path || !count) return fail(W12_ERR_INVALID_ARG, "path or count is NULL");
+  char err[256];
+  if (entries && max_entries < 0) return fail(W12_ERR_INVALID_ARG, "max_entries < 0");
+  int32_t n = 0;
+  if (w12::file_index(path, &n, nullptr, 0, err, sizeof(err))) return fail(W12_ERR_IO, "%s", err);
+  *count = n;
+  if (!entries) return ok();
+  if (n > max_entries) return fail(W12_ERR_INVALID_ARG, "file holds %d tensors, room for %d", n, max_entries);
+  if (w12::file_index(path, &n, entries, max_entries, err, sizeof(err))) return fail(W12_ERR_IO, "%s", err);
+  return ok();
+}
+
+int w12_file_load(const char* path, int32_t count, const int32_t* which, const w12_tensor* dst, void* staging,
+                  uint64_t staging_bytes, const uint16_t* const* refs, const int64_t* ldr,
+                  unsigned long long* d_results, hipStream_t stream) {
+  if (!path || !which || !dst) return fail(W12_ERR_INVALID_ARG, "path, which or dst is NULL");
+  if (count < 1) return fail(W12_ERR_INVALID_ARG, "count=%d must be at least 1", count);
+  if (!staging || staging_bytes < 512) return fail(W12_ERR_INVALID_ARG, "staging must hold at least 512 bytes");
+  char err[256];
+  int32_t n = 0;
+  if (w12::file_index(path, &n, nullptr, 0, err, sizeof(err))) return fail(W12_ERR_IO, "%s", err);
+  std::vector<w12_file_entry> idx(n);
+  if (n && w12::file_index(path, &n, idx.data(), n, err, sizeof(err))) return fail(W12_ERR_IO, "%s", err);
+  for (int i = 0; i < count; ++i) {
+    if (which[i] < 0 || which[i] >= n) return fail(W12_ERR_INVALID_ARG, "which[%d]=%d outside 0..%d", i, which[i], n - 1);
+    int rc = check_tensor(&dst[i]);
+    if (rc) return item_fail(rc, i);
+    const w12_file_entry& e = idx[which[i]];
+    if (e.N != dst[i].N || e.K != dst[i].K || e.layout != dst[i].layout || e.num_escapes != dst[i].num_escapes)
+      return fail(W12_ERR_INVALID_ARG, "item %d: descriptor does not match file entry %d (%s)", i, which[i], e.name);
+    if (refs && refs[i]) {
+      if (!ldr) return fail(W12_ERR_INVALID_ARG, "ldr is NULL");
+      if ((rc = check_bf16_matrix(refs[i], ldr[i], dst[i].K, "ref"))) return item_fail(rc, i);
+      if (!d_results) return fail(W12_ERR_INVALID_ARG, "d_results is NULL");
+      if (!aligned(d_results, 8)) return fail(W12_ERR_MISALIGNED, "d_results must be 8-byte aligned");
+    }
+  }
+  const int rc = w12::file_load(path, count, which, dst, staging, staging_bytes, refs, ldr, d_results, stream, err,
+                                sizeof(err));
+  if (rc == -1) return fail(W12_ERR_IO, "%s", err);
+  if (rc) return fail(W12_ERR_HIP, "%s", err);
+  return ok();
+}
+
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {
   if (N < 1 || K < 1 || E < 0) return -1.0;
   const double nk = (double)N * (double)K;
@@ -277,6 +337,7 @@ const char* w12_status_string(int status) {
     case W12_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case W12_ERR_HIP: return "HIP error";
     case W12_ERR_MISALIGNED: return "misaligned pointer or pitch";
+    case W12_ERR_IO: return "checkpoint file error";
     default: return "unknown status";
   }
 }

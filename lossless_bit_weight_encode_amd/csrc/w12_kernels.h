@@ -57,4 +57,15 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream);
 
+// Checkpoint files (host side; w12_file.cpp).  Return 0, -1 for an I/O or format error, -2
+// for a HIP error, with a message in err.
+uint64_t file_tensor_bytes(int32_t N, int32_t K, int64_t E);
+int file_write(const char* path, int32_t count, const char* const* names, const w12_tensor* host_tensors, char* err,
+               size_t errn);
+int file_index(const char* path, int32_t* count, w12_file_entry* entries, int32_t max_entries, char* err,
+               size_t errn);
+int file_load(const char* path, int32_t count, const int32_t* which, const w12_tensor* dst, void* staging,
+              uint64_t staging_bytes, const uint16_t* const* refs, const int64_t* ldr, unsigned long long* d_results,
+              hipStream_t stream, char* err, size_t errn);
+
 }  // namespace w12
