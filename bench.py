@@ -163,7 +163,7 @@ def main():
     y_dev = {nm: torch.empty(m_step, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names}
     ws = {nm: w12.gemm_workspace(m_step, *S.LAYER_SHAPES[nm]) for nm in names}
 
-    # HIP events bracket every gate_up launch of the timed steps (same stream as the launch);
+    # HIP events bracket every gate_up launch of the roofline pass (same stream as the launch);
     # the host enqueues a step in well under the step's GPU time, so the stream is never idle
     # between an event and its kernel.
     ev_pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -183,8 +183,12 @@ def main():
     for i in range(args.warmup):
         layer_step(i)
     torch.cuda.synchronize()
-    rec["on"] = True
+    # the headline: K steps with nothing but the GEMM launches on the stream
     t_step = timed(layer_step, args.steps, stream)
+    # then K more steps with HIP events around every gate_up launch, for the per-launch roofline
+    # (each event record is a marker packet on the stream and lengthens the step it sits in)
+    rec["on"] = True
+    t_step_instr = timed(layer_step, args.steps, stream)
     rec["on"] = False
     gate_us = [a.elapsed_time(b) * 1e3 for a, b in ev_pairs]
     weight_bytes = sum(2 * n * k for n, k in (S.LAYER_SHAPES[nm] for nm in names))
@@ -216,6 +220,7 @@ def main():
             "bytes_moved_frac_of_8TBps": round(moved / t_step / 1e6 / HBM_PEAK_GBPS, 4),
             "byte_floor_us": round(sum(byte_floor_us(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes)
                                        for nm in names), 2),
+            "ms_per_step_with_gate_up_events": round(t_step_instr, 5),
             "rotated_copies": len(copies),
             "inputs_sha256": {nm: S.sha256(layer[nm])[:16] for nm in names},
         },

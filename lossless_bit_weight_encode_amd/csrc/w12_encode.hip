@@ -97,26 +97,45 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
 }
 
 // esc_ptr[0] = 0 and an inclusive scan of the counts in esc_ptr[1..N] (one work-group).
-__global__ __launch_bounds__(1024) void k_scan_counts(uint32_t* __restrict__ esc_ptr, int32_t N) {
-  __shared__ uint32_t part[1024];
+// Thread t owns the contiguous stretch [1 + t per, 1 + (t+1) per); it loads its counts
+// kScanBatch at a time with every load of a batch issued before any is used (for N up to
+// 49152 the whole stretch is one batch and stays in registers between the two passes).
+constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 48;
+__global__ __launch_bounds__(kScanThreads) void k_scan_counts(uint32_t* __restrict__ esc_ptr, int32_t N) {
+  __shared__ uint32_t part[kScanThreads];
   const int t = threadIdx.x;
-  const int64_t per = ((int64_t)N + 1023) / 1024;
+  const int64_t per = ((int64_t)N + kScanThreads - 1) / kScanThreads;
   const int64_t lo = 1 + (int64_t)t * per;
   const int64_t hi = (lo + per < (int64_t)N + 1) ? lo + per : (int64_t)N + 1;
+  uint32_t v[kScanBatch];
   uint32_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += esc_ptr[i];
+  for (int64_t i0 = lo; i0 < hi; i0 += kScanBatch) {
+#pragma unroll
+    for (int k = 0; k < kScanBatch; ++k) v[k] = (i0 + k < hi) ? esc_ptr[i0 + k] : 0u;
+#pragma unroll
+    for (int k = 0; k < kScanBatch; ++k) s += v[k];
+  }
   part[t] = s;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const uint32_t v = (t >= off) ? part[t - off] : 0u;
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const uint32_t x = (t >= off) ? part[t - off] : 0u;
     __syncthreads();
-    part[t] += v;
+    part[t] += x;
     __syncthreads();
   }
   uint32_t run = (t > 0) ? part[t - 1] : 0u;
-  for (int64_t i = lo; i < hi; ++i) {
-    run += esc_ptr[i];
-    esc_ptr[i] = run;
+  const bool one_batch = per <= kScanBatch;   // v still holds the stretch
+  for (int64_t i0 = lo; i0 < hi; i0 += kScanBatch) {
+    if (!one_batch) {
+#pragma unroll
+      for (int k = 0; k < kScanBatch; ++k) v[k] = (i0 + k < hi) ? esc_ptr[i0 + k] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanBatch; ++k) {
+      run += v[k];
+      if (i0 + k < hi) esc_ptr[i0 + k] = run;
+    }
   }
   if (t == 0) esc_ptr[0] = 0;
 }
@@ -222,7 +241,7 @@ hipError_t launch_encode_count(const uint16_t* W, int32_t N, int32_t K, int64_t 
                      esc_ptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(1024), 0, stream, esc_ptr, N);
+  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(kScanThreads), 0, stream, esc_ptr, N);
   return hipGetLastError();
 }
 

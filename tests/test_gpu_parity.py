@@ -35,6 +35,8 @@ CASES = {
     "single_1x16": lambda: S.random_bits_matrix(np.random.default_rng(4), 1, 16, "wide"),
     "heavy_64x2048": lambda: S.heavy_tail_weights(1000, 64, 2048),
     "all_escapes_20x96": lambda: np.zeros((20, 96), dtype=np.uint16),
+    # more channels than one pass of the escape-count scan keeps in registers
+    "tall_100003x16": lambda: S.random_bits_matrix(np.random.default_rng(6), 100003, 16, "wide"),
 }
 
 _cache = {}
