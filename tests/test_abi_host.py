@@ -228,3 +228,29 @@ def test_gemm_group_workspace_covers_counters_and_partials(m):
     one = L._c_u64()
     assert w12.lib().w12_gemm_group_workspace_size(m, 1, _items(d[2:3], m), ctypes.byref(one)) == 0
     assert one.value <= need.value
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """Without libw12.so the binding raises; there is no other code path."""
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent" / "libw12.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        L.lib()
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    w = torch.zeros(16, 16, dtype=torch.int16)
+    with pytest.raises(ValueError, match="GPU"):
+        w12.encode(w)
+    with pytest.raises(ValueError, match="GPU"):
+        w12.gemm(torch.zeros(1, 16, dtype=torch.int16), None)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
