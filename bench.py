@@ -74,6 +74,34 @@ def timed(fn, iters, stream):
     return start.elapsed_time(stop) / iters
 
 
+def timed_blocks(fn, iters, stream, blocks=5):
+    """Average milliseconds per call over iters calls (one synchronisation on each side), plus the
+    per-call means of `blocks` consecutive blocks of calls, from events recorded between blocks."""
+    nb = max(1, min(blocks, iters))
+    bounds = [round(i * iters / nb) for i in range(nb + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for b in range(nb):
+        for i in range(bounds[b], bounds[b + 1]):
+            fn(i)
+        ev[b + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[b].elapsed_time(ev[b + 1]) / (bounds[b + 1] - bounds[b]) for b in range(nb)]
+    return ev[0].elapsed_time(ev[nb]) / iters, per
+
+
+def ci95(samples):
+    """Median and the half-width of a t-based 95% confidence interval of the mean."""
+    import statistics
+    n = len(samples)
+    med = statistics.median(samples)
+    if n < 2:
+        return med, None
+    t = {2: 12.71, 3: 4.30, 4: 3.18, 5: 2.78, 6: 2.57, 7: 2.45, 8: 2.36, 9: 2.31, 10: 2.26}.get(n, 2.0)
+    return med, t * statistics.stdev(samples) / n ** 0.5
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,8 +211,9 @@ def main():
     for i in range(args.warmup):
         layer_step(i)
     torch.cuda.synchronize()
-    # the headline: K steps with nothing but the GEMM launches on the stream
-    t_step = timed(layer_step, args.steps, stream)
+    # the headline: K steps with nothing but the GEMM launches on the stream (events only at the
+    # boundaries of 5 consecutive blocks of steps, for the spread)
+    t_step, block_ms = timed_blocks(layer_step, args.steps, stream)
     # then K more steps with HIP events around every gate_up launch, for the per-launch roofline
     # (each event record is a marker packet on the stream and lengthens the step it sits in)
     rec["on"] = True
@@ -221,6 +250,9 @@ def main():
             "byte_floor_us": round(sum(byte_floor_us(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes)
                                        for nm in names), 2),
             "ms_per_step_with_gate_up_events": round(t_step_instr, 5),
+            "ms_per_step_block_median": round(ci95(block_ms)[0], 5),
+            "ms_per_step_ci95_halfwidth": None if ci95(block_ms)[1] is None else round(ci95(block_ms)[1], 5),
+            "step_blocks": len(block_ms),
             "rotated_copies": len(copies),
             "inputs_sha256": {nm: S.sha256(layer[nm])[:16] for nm in names},
         },
