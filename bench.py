@@ -328,6 +328,20 @@ def main():
     }
     log(f"[bench] Q-pass layer step {t_q * 1e3:.1f} us -> {weight_bytes / t_q / 1e6:.1f} weight-GB/s")
 
+    # ---- hot cache: each layer GEMM at M=16 re-reading one copy (labelled; not the headline) ----
+    hot = {}
+    for nm in names:
+        n, k = S.LAYER_SHAPES[nm]
+        f = lambda i: w12.gemm(x_dev[(nm, m_step)], enc[nm], y=y_dev[nm], ws=ws[nm], stream=stream)
+        for i in range(3):
+            f(i)
+        t = timed(f, 30, stream)
+        ab = alg_bytes(n, k, m_step, enc[nm].num_escapes)
+        hot[nm] = {"us": round(t * 1e3, 2), "moved_GBps": round(ab / t / 1e6, 1),
+                   "w12_MB": round(enc[nm].nbytes() / 1e6, 1)}
+    out["hot_cache"] = {"what": "the same encoded copy launched 30 times in a row at M=16: matrices under the "
+                                "256 MB Infinity Cache are served from it", **hot}
+
     # ---- tree-verify M sweep on gate_up and down ----
     if not args.no_sweep:
         sweep = {}
@@ -722,30 +736,43 @@ def summarize_counters(fetch_csv, write_csv):
 
 
 def cpu_baseline(layer, enc):
-    """The oracle's decode + FP64 GEMM of gate_up at M=16 (the whole matrix), timed 3 times."""
+    """The oracle's decode + FP64 GEMM of gate_up at M=16 (the whole matrix), timed 3 times on all
+    host cores, once on one thread; and the oracle's encode of the same matrix, timed once."""
     from oracle import w12_oracle as O
     w = layer["gate_up"]
     n, k = w.shape
     log("[bench] cpu baseline: oracle encode of gate_up")
+    t0 = time.perf_counter()
     ref = O.encode(w)
+    t_enc = time.perf_counter() - t0
     x = S.activations(16, k, S.x_seed(16, k))
-    times = []
-    for _ in range(3):
+
+    def run():
         t0 = time.perf_counter()
         wd = O.decode(ref)
         O.gemm_reference(x, wd)
-        times.append(time.perf_counter() - t0)
+        return time.perf_counter() - t0
+
+    times = []
+    for _ in range(3):
+        times.append(run())
         log(f"[bench] cpu baseline rep {times[-1]:.2f}s")
     t = float(np.median(times))
+    blas_threads, t1 = None, None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with threadpool_limits(limits=1):
+            t1 = run()
+        log(f"[bench] cpu baseline one thread {t1:.2f}s")
     except Exception:
-        blas_threads = None
+        pass
     return {
         "value": round(2 * n * k / t / 1e9, 3), "unit": "GB/s", "cores": len(os.sched_getaffinity(0)),
         "blas_threads": blas_threads, "kind": "oracle",
         "sample": f"gate_up {n}x{k}, M=16: oracle decode + FP64 GEMM, median of 3 runs ({t:.2f} s each)",
+        "one_thread": None if t1 is None else {"s": round(t1, 3), "GBps": round(2 * n * k / t1 / 1e9, 3)},
+        "oracle_encode": {"s": round(t_enc, 3), "GBps": round(2 * n * k / t_enc / 1e9, 3)},
     }
 
 
