@@ -64,6 +64,16 @@ def test_encode_matches_oracle(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("blocks", [0, 1])
+def test_encode_both_emit_kernels(monkeypatch, name, blocks):
+    """Record emission by one wave per row and by one work-group per 16-row block (chosen by the
+    number of row blocks; W12_EMIT_BLOCKS forces either) gives the oracle's encoding."""
+    monkeypatch.setenv("W12_EMIT_BLOCKS", str(blocks))
+    w, ref = case(name)
+    assert_encode_equal(w12.encode(dev_weights(w)), ref)
+
+
+@pytest.mark.parametrize("name", list(CASES))
 def test_verify_and_decode_bit_exact(name):
     w, _ = case(name)
     wd = dev_weights(w)
