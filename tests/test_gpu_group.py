@@ -153,3 +153,40 @@ def test_group_layer_full_size(m):
         bad, worst = O.gemm_check(xs[i], lay[nm][rows], yh[:, rows])
         assert bad == 0, f"{nm} M={m}: {bad} sampled outputs outside tolerance (worst rel {worst:.3g})"
         assert np.isfinite(yh).all()
+
+
+@pytest.mark.parametrize("m", [1, 16, 40])
+def test_group_deterministic_poisoned_workspace_and_canaries(monkeypatch, m):
+    """20 grouped launches bitwise identical, with the partial region of the workspace
+    NaN-poisoned before every launch (a read of a partial never written would show) and canary
+    values around every Y (nothing written outside Y).  A small grid makes most tiles split."""
+    monkeypatch.setenv("W12_MAX_GRID", "7")
+    names = ALL[:5]
+    ws_, ts, xs = [], [], []
+    for i, nm in enumerate(names):
+        w, t, _ = member(nm)
+        ws_.append(w)
+        ts.append(t)
+        xs.append(S.activations(m, w.shape[1], 9000 + 17 * i + m))
+    xd = [to_dev(x) for x in xs]
+    canary = -12345.678
+    bufs = [torch.full((m + 3, t.n + 11), canary, dtype=torch.float32, device="cuda") for t in ts]
+    ys = [b[:m, :t.n] for b, t in zip(bufs, ts)]
+    ws = w12.gemm_group_workspace(m, ts)
+    cb = (4 * sum(-(-(-(-t.n // 16)) // 4) for t in ts) + 255) // 256 * 256
+    outs = []
+    for _ in range(20):
+        ws[cb:].view(torch.uint8).fill_(0xFF)   # NaN patterns in every partial slot
+        w12.gemm_group(xd, ts, ys, ws=ws)
+        torch.cuda.synchronize()
+        outs.append([y.cpu().numpy().view(np.uint32).copy() for y in ys])
+        assert int(ws[:cb].count_nonzero()) == 0, "arrival counters must return to zero"
+    for o in outs[1:]:
+        for a, b in zip(o, outs[0]):
+            assert np.array_equal(a, b)
+    for i, (b, t) in enumerate(zip(bufs, ts)):
+        bh = b.cpu().numpy()
+        assert (bh[:m, t.n:] == np.float32(canary)).all(), f"item {i}: write past N"
+        assert (bh[m:, :] == np.float32(canary)).all(), f"item {i}: write past M"
+        bad, worst = O.gemm_check(xs[i], ws_[i], outs[0][i].view(np.float32))
+        assert bad == 0, f"item {i}: {bad} outputs outside tolerance"
