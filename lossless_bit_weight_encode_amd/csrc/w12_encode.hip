@@ -148,14 +148,87 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// The 16 weights of chunk c of one row (a wave holds one row, lane l chunk c): their values,
+// the mask of those that escape, and the packed hi bytes (16) and lo nibbles (8 bytes) of their
+// records.  Lanes past the row (inactive) and rows past N (padding) give record 0 and no escape.
+__device__ __forceinline__ void chunk_records(const uint16_t* __restrict__ row, int32_t K, int64_t c, bool active,
+                                              bool real, uint32_t b, uint32_t v[16], uint32_t& escmask, uint4& hi16,
+                                              uint2& lo8) {
+  int valid = 0;
+  if (active && real) {
+    const int64_t rem = (int64_t)K - c * kChunkK;
+    valid = rem >= kChunkK ? kChunkK : (int)rem;
+    uint4 a, bq;
+    load16_bf16(row + c * kChunkK, valid, a, bq);
+    const uint32_t w2[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = w2[i] & 0xFFFFu;
+      v[2 * i + 1] = w2[i] >> 16;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = 0;
+  }
+  uint32_t rec[16];
+  escmask = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t e = (v[j] >> 7) & 0xFFu;
+    const bool in = (e >= b) && (e <= b + 15u);
+    const bool isreal = j < valid;
+    rec[j] = (in && isreal) ? (((v[j] >> 15) << 11) | ((e - b) << 7) | (v[j] & 0x7Fu)) : 0u;
+    if (isreal && !in) escmask |= 1u << j;
+  }
+  uint32_t hw[4], lw[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    hw[i] = (rec[4 * i] >> 4) | ((rec[4 * i + 1] >> 4) << 8) | ((rec[4 * i + 2] >> 4) << 16) |
+            ((rec[4 * i + 3] >> 4) << 24);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t byte = ((rec[8 * d + i] & 0xFu) << 4) | (rec[8 * d + 4 + i] & 0xFu);
+      x |= byte << (8 * i);
+    }
+    lw[d] = x;
+  }
+  hi16 = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  lo8 = make_uint2(lw[0], lw[1]);
+}
+
+// Append the chunk's escapes to the row's list in ascending k: every lane counts its escapes, and
+// a wavefront prefix sum (one ballot per bit of the count) gives its slot after the row's running
+// offset, which then advances by the wave's total.  Called by every lane of the wave.
+__device__ __forceinline__ void chunk_escapes(const uint32_t v[16], uint32_t escmask, int64_t c, uint32_t& slot,
+                                              uint32_t* __restrict__ esc, uint32_t num_esc) {
+  const uint32_t cnt = __builtin_popcount(escmask);
+  uint32_t prefix = 0, total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit) {
+    const uint64_t m = __ballot((cnt >> bit) & 1u);
+    prefix += lanes_below(m) << bit;
+    total += (uint32_t)__popcll(m) << bit;
+  }
+  uint32_t o = slot + prefix;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (escmask & (1u << j)) {
+      if (o < num_esc) esc[o] = ((uint32_t)(c * kChunkK + j) << 16) | v[j];
+      ++o;
+    }
+  }
+  slot += total;
+}
+
 // One work-group per row block; wave r encodes row 16 rb + r, lane l chunk c0 + l (16
 // consecutive k).  The records of the block's 64 chunks of an iteration are staged in LDS in
 // plane order ([chunk][row][16 bytes] and [chunk][row][8 bytes]) and stored as one contiguous
-// 16 KB hi run and one 8 KB lo run, every lane writing adjacent bytes.  Escapes are compacted
-// per row in ascending k: every lane counts its escapes, a wavefront prefix sum (one ballot
-// per bit of the count) gives its slot after the channel's running offset.
+// 16 KB hi run and one 8 KB lo run, every lane writing adjacent bytes.
 __global__ __launch_bounds__(kEmitThreads) void k_encode_emit_blocks(
-    const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, int64_t Np, int64_t Kc,
+    const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, int64_t Kc,
     const uint8_t* __restrict__ base, const uint32_t* __restrict__ esc_ptr, uint8_t* __restrict__ hi,
     uint8_t* __restrict__ lo, uint32_t* __restrict__ esc, uint32_t num_esc) {
   __shared__ uint4 s_hi[kWave * kRowsPerBlock];   // [chunk][row]
@@ -170,91 +243,30 @@ __global__ __launch_bounds__(kEmitThreads) void k_encode_emit_blocks(
   const uint16_t* row = W + (real ? n : 0) * ldw;
   for (int64_t c0 = 0; c0 < Kc; c0 += kWave) {
     const int64_t c = c0 + lane;
-    const bool active = c < Kc;
-    uint32_t v[16];
-    int valid = 0;
-    if (active && real) {
-      const int64_t rem = (int64_t)K - c * kChunkK;
-      valid = rem >= kChunkK ? kChunkK : (int)rem;
-      uint4 a, bq;
-      load16_bf16(row + c * kChunkK, valid, a, bq);
-      const uint32_t w2[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = w2[i] & 0xFFFFu;
-        v[2 * i + 1] = w2[i] >> 16;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0;
-    }
-    uint32_t rec[16];
-    uint32_t escmask = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t e = (v[j] >> 7) & 0xFFu;
-      const bool in = (e >= b) && (e <= b + 15u);
-      const bool isreal = j < valid;
-      rec[j] = (in && isreal) ? (((v[j] >> 15) << 11) | ((e - b) << 7) | (v[j] & 0x7Fu)) : 0u;
-      if (isreal && !in) escmask |= 1u << j;
-    }
-    {
-      uint32_t hw[4], lw[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hw[i] = (rec[4 * i] >> 4) | ((rec[4 * i + 1] >> 4) << 8) | ((rec[4 * i + 2] >> 4) << 16) |
-                ((rec[4 * i + 3] >> 4) << 24);
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t byte = ((rec[8 * d + i] & 0xFu) << 4) | (rec[8 * d + 4 + i] & 0xFu);
-          x |= byte << (8 * i);
-        }
-        lw[d] = x;
-      }
-      s_hi[lane * kRowsPerBlock + r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      s_lo[lane * kRowsPerBlock + r] = make_uint2(lw[0], lw[1]);
-    }
-    if (real) {
-      const uint32_t cnt = __builtin_popcount(escmask);
-      uint32_t prefix = 0, total = 0;
-#pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
-        const uint64_t m = __ballot((cnt >> bit) & 1u);
-        prefix += lanes_below(m) << bit;
-        total += (uint32_t)__popcll(m) << bit;
-      }
-      uint32_t o = slot + prefix;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (escmask & (1u << j)) {
-          if (o < num_esc) esc[o] = ((uint32_t)(c * kChunkK + j) << 16) | v[j];
-          ++o;
-        }
-      }
-      slot += total;
-    }
+    uint32_t v[16], escmask;
+    uint4 h;
+    uint2 l;
+    chunk_records(row, K, c, c < Kc, real, b, v, escmask, h, l);
+    s_hi[lane * kRowsPerBlock + r] = h;
+    s_lo[lane * kRowsPerBlock + r] = l;
+    if (real) chunk_escapes(v, escmask, c, slot, esc, num_esc);
     __syncthreads();
     // the block's chunks c0 .. c0 + nc - 1 are contiguous in both planes
     const int64_t nc = Kc - c0 < kWave ? Kc - c0 : kWave;
-    const int t = threadIdx.x;   // hi: one 16-byte piece per thread
-    if (t < nc * kRowsPerBlock)
+    const int t = threadIdx.x;   // one 16-byte hi piece and one 8-byte lo piece per thread
+    if (t < nc * kRowsPerBlock) {
       *reinterpret_cast<uint4*>(hi + hi_offset(rb, c0, Kc, 0) + 16 * t) = s_hi[t];
-    if (t < nc * kRowsPerBlock)
       *reinterpret_cast<uint2*>(lo + lo_offset(rb, c0, Kc, 0) + 8 * t) = s_lo[t];
+    }
     __syncthreads();
   }
 }
 
 constexpr int kEmitRowWaves = 4;
 
-
 // One wave per (padded) row; lane l owns chunk c0 + l (16 consecutive k).  Records go straight
-// to the hi/lo planes (16 and 8 bytes per lane, 256 and 128 bytes apart); escapes are compacted
-// as in k_encode_emit_blocks.  Used when there are too few row blocks to fill the GPU with
-// block work-groups.
+// to the hi/lo planes (16 and 8 bytes per lane, 256 and 128 bytes apart).  Used when there are
+// too few row blocks to fill the GPU with block work-groups.
 __global__ __launch_bounds__(kEmitRowWaves * kWave) void k_encode_emit_rows(
     const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, int64_t Np, int64_t Kc,
     const uint8_t* __restrict__ base, const uint32_t* __restrict__ esc_ptr, uint8_t* __restrict__ hi,
@@ -271,71 +283,15 @@ __global__ __launch_bounds__(kEmitRowWaves * kWave) void k_encode_emit_rows(
   for (int64_t c0 = 0; c0 < Kc; c0 += kWave) {
     const int64_t c = c0 + lane;
     const bool active = c < Kc;
-    uint32_t v[16];
-    int valid = 0;
-    if (active && real) {
-      const int64_t rem = (int64_t)K - c * kChunkK;
-      valid = rem >= kChunkK ? kChunkK : (int)rem;
-      uint4 a, bq;
-      load16_bf16(row + c * kChunkK, valid, a, bq);
-      const uint32_t w2[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = w2[i] & 0xFFFFu;
-        v[2 * i + 1] = w2[i] >> 16;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = 0;
-    }
-    uint32_t rec[16];
-    uint32_t escmask = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t e = (v[j] >> 7) & 0xFFu;
-      const bool in = (e >= b) && (e <= b + 15u);
-      const bool isreal = j < valid;
-      rec[j] = (in && isreal) ? (((v[j] >> 15) << 11) | ((e - b) << 7) | (v[j] & 0x7Fu)) : 0u;
-      if (isreal && !in) escmask |= 1u << j;
-    }
+    uint32_t v[16], escmask;
+    uint4 h;
+    uint2 l;
+    chunk_records(row, K, c, active, real, b, v, escmask, h, l);
     if (active) {
-      uint32_t hw[4], lw[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hw[i] = (rec[4 * i] >> 4) | ((rec[4 * i + 1] >> 4) << 8) | ((rec[4 * i + 2] >> 4) << 16) |
-                ((rec[4 * i + 3] >> 4) << 24);
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t byte = ((rec[8 * d + i] & 0xFu) << 4) | (rec[8 * d + 4 + i] & 0xFu);
-          x |= byte << (8 * i);
-        }
-        lw[d] = x;
-      }
-      *reinterpret_cast<uint4*>(hi + hi_offset(rb, c, Kc, r)) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint2*>(lo + lo_offset(rb, c, Kc, r)) = make_uint2(lw[0], lw[1]);
+      *reinterpret_cast<uint4*>(hi + hi_offset(rb, c, Kc, r)) = h;
+      *reinterpret_cast<uint2*>(lo + lo_offset(rb, c, Kc, r)) = l;
     }
-    if (real) {
-      const uint32_t cnt = __builtin_popcount(escmask);
-      uint32_t prefix = 0, total = 0;
-#pragma unroll
-      for (int bit = 0; bit < 5; ++bit) {
-        const uint64_t m = __ballot((cnt >> bit) & 1u);
-        prefix += lanes_below(m) << bit;
-        total += (uint32_t)__popcll(m) << bit;
-      }
-      uint32_t o = slot + prefix;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (escmask & (1u << j)) {
-          if (o < num_esc) esc[o] = ((uint32_t)(c * kChunkK + j) << 16) | v[j];
-          ++o;
-        }
-      }
-      slot += total;
-    }
+    if (real) chunk_escapes(v, escmask, c, slot, esc, num_esc);
   }
 }
 
@@ -359,8 +315,8 @@ hipError_t launch_encode_emit(const uint16_t* W, int64_t ldw, const w12_tensor* 
   const int force = env_int("W12_EMIT_BLOCKS", -1);
   const bool blocks = force >= 0 ? force != 0 : Nb >= 4 * (int64_t)device_cus();
   if (blocks) {
-    hipLaunchKernelGGL(k_encode_emit_blocks, dim3((unsigned)Nb), dim3(kEmitThreads), 0, stream, W, t->N, t->K, ldw, Np,
-                       Kc, t->base, t->esc_ptr, t->hi, t->lo, t->esc, (uint32_t)t->num_escapes);
+    hipLaunchKernelGGL(k_encode_emit_blocks, dim3((unsigned)Nb), dim3(kEmitThreads), 0, stream, W, t->N, t->K, ldw, Kc,
+                       t->base, t->esc_ptr, t->hi, t->lo, t->esc, (uint32_t)t->num_escapes);
   } else {
     const unsigned grid = (unsigned)((Np + kEmitRowWaves - 1) / kEmitRowWaves);
     hipLaunchKernelGGL(k_encode_emit_rows, dim3(grid), dim3(kEmitRowWaves * kWave), 0, stream, W, t->N, t->K, ldw, Np,
