@@ -113,6 +113,11 @@ def main():
     ap.add_argument("--no-full-model", action="store_true", help="skip the 64-layer weight stream")
     ap.add_argument("--model-layers", type=int, default=S.FULL_MODEL_LAYERS)
     ap.add_argument("--only-layer", action="store_true", help="time only the layer steps (for profiling)")
+    ap.add_argument("--only-group", action="store_true",
+                    help="time only the grouped layer steps, one w12_gemm_group launch each (for profiling)")
+    ap.add_argument("--summarize-group-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of --only-group into the grouped-launch "
+                         "kernel-time summary under profiles/")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the layer steps, run one torch elementwise kernel that reads and writes exactly "
                          "256 MiB (the plain kernel of known size against which HBM byte counters are scaled)")
@@ -135,6 +140,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_group_trace:
+        summarize_group_trace(*args.summarize_group_trace)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
@@ -190,6 +198,22 @@ def main():
     copies = [enc] + [{nm: clone_tensor(enc[nm]) for nm in names} for _ in range(args.copies - 1)]
     y_dev = {nm: torch.empty(m_step, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names}
     ws = {nm: w12.gemm_workspace(m_step, *S.LAYER_SHAPES[nm]) for nm in names}
+    if args.only_group:
+        xs_o = [x_dev[(nm, m_step)] for nm in names]
+        ys_o = [y_dev[nm] for nm in names]
+        ws_o = w12.gemm_group_workspace(m_step, [enc[nm] for nm in names])
+
+        def group_only(i):
+            c = copies[i % len(copies)]
+            w12.gemm_group(xs_o, [c[nm] for nm in names], ys_o, ws=ws_o, stream=stream)
+
+        for i in range(args.warmup):
+            group_only(i)
+        t_o = timed(group_only, args.steps, stream)
+        moved_o = sum(alg_bytes(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes) for nm in names)
+        print(json.dumps({"what": "grouped layer step (qkv, o_proj, gate_up, down at M=16, one launch)",
+                          "ms_per_step": round(t_o, 5), "bytes_moved_GBps": round(moved_o / t_o / 1e6, 1)}))
+        return
 
     # HIP events bracket every gate_up launch of the roofline pass (same stream as the launch);
     # the host enqueues a step in well under the step's GPU time, so the stream is never idle
@@ -683,6 +707,38 @@ def summarize_trace(stats_csv, trace_csv, command):
         lines.append(f"| {nm} | `{rows[0]['Kernel_Name'].split('(')[0]}` | {len(d)} | {d.mean():.2f} | "
                      f"{np.median(d):.2f} | {d.min():.2f} | {d.max():.2f} |")
     path = os.path.join(ROOT, "profiles", "gemm_layer_M16_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_group_trace(stats_csv, trace_csv, command):
+    """Kernel-time summary of a profiled --only-group run: rocprofv3's per-kernel stats and the
+    grouped GEMM launches (one per layer step: qkv, o_proj, gate_up and down together)."""
+    import csv
+    with open(stats_csv) as f:
+        stats = list(csv.DictReader(f))
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    grp = [r for r in trace if "k_gemm_group" in r["Kernel_Name"]]
+    d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in grp])
+    moved = 0
+    for nm in S.LAYER_ORDER:
+        n, k = S.LAYER_SHAPES[nm]
+        moved += 1.5 * n * k   # the records dominate; exact bytes are in the bench line
+    lines = ["# W12 grouped GEMM: one dense decoder layer (hidden 5120) in one launch, M=16, MI355X", "",
+             "Command (run from the repository root):", "", "```", command, "```", "",
+             "## rocprofv3 --stats (all kernels of the run)", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines += ["", "## Grouped launches (kernel trace)", "",
+              "| kernel | launches | avg us | median us | min us | max us | record bytes / avg time |",
+              "|---|---|---|---|---|---|---|",
+              f"| `{grp[0]['Kernel_Name'].split('(')[0]}` | {len(d)} | {d.mean():.2f} | {np.median(d):.2f} | "
+              f"{d.min():.2f} | {d.max():.2f} | {moved / d.mean() / 1e3:.0f} GB/s |"]
+    path = os.path.join(ROOT, "profiles", "gemm_group_layer_M16_kernel_trace.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
