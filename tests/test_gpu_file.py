@@ -22,6 +22,7 @@ def _sources():
         "heavy": S.heavy_tail_weights(1000, 64, 2048),
         "zeros": np.zeros((20, 96), dtype=np.uint16),
         "ragged": S.random_bits_matrix(np.random.default_rng(3), 17, 33, "wide"),
+        "no_escapes": S.to_bf16_bits(1.0 + torch.rand(32, 256, generator=torch.Generator().manual_seed(8))),
     }
 
 

@@ -37,6 +37,8 @@ CASES = {
     "all_escapes_20x96": lambda: np.zeros((20, 96), dtype=np.uint16),
     # more channels than one pass of the escape-count scan keeps in registers
     "tall_100003x16": lambda: S.random_bits_matrix(np.random.default_rng(6), 100003, 16, "wide"),
+    # every weight in [1, 2): one binade, no escape at all (E = 0, no escape array)
+    "no_escapes_64x512": lambda: S.to_bf16_bits(1.0 + torch.rand(64, 512, generator=torch.Generator().manual_seed(8))),
 }
 
 _cache = {}
@@ -156,7 +158,7 @@ def test_verify_reports_corruption():
 # ---------------------------------------------------------------------------------------
 
 GEMM_SHAPES = ["tiny_256x512", "wide_37x1000", "gauss_300x4096", "uniform_bits_100x520", "ragged_17x33",
-               "single_1x16", "heavy_64x2048", "all_escapes_20x96"]
+               "single_1x16", "heavy_64x2048", "all_escapes_20x96", "no_escapes_64x512"]
 GEMM_M = [1, 2, 3, 5, 8, 9, 16, 17, 24, 32, 33, 48, 63, 64, 65, 100, 128]
 
 
