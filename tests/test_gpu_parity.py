@@ -359,3 +359,26 @@ def test_gemm_writes_only_y(m):
     assert (b[m:, :] == np.float32(canary)).all()
     bad, _ = O.gemm_check(S.activations(m, k, 9), w, b[:m, :n])
     assert bad == 0
+
+
+@pytest.mark.parametrize("m", [1, 2, 16, 40, 100])
+def test_gemm_max_k(m):
+    """K = 65536 (the largest K: escape entries keep k in 16 bits), where a lane's serial chain of
+    products is longest."""
+    w = S.layer_matrix(torch.Generator().manual_seed(21), 40, 65536)
+    x = S.activations(m, 65536, 700 + m)
+    t = w12.encode(to_dev(w))
+    y = w12.gemm(to_dev(x), t).cpu().numpy()
+    bad, worst = O.gemm_check(x, w, y)
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
+
+
+@pytest.mark.parametrize("m", [1025, 4096])
+def test_gemm_large_m(m):
+    """Many m tiles of the wide kernel, up to the largest M the library accepts."""
+    w, _ = case("heavy_64x2048")
+    x = S.activations(m, w.shape[1], 800 + m)
+    t = w12.encode(dev_weights(w))
+    y = w12.gemm(to_dev(x), t).cpu().numpy()
+    bad, worst = O.gemm_check(x, w, y)
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
