@@ -251,7 +251,7 @@ def main():
         f"{moved / t_step / 1e6:.1f} GB/s moved")
 
     out = {
-        "metric": "w12_gemm weight-GB/s",
+        "metric": "w12_gemm weight-GB/s and % of HBM peak at M=1..64; bits/weight",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -271,6 +271,7 @@ def main():
             "bytes_moved_per_step": int(moved),
             "bytes_moved_GBps": round(moved / t_step / 1e6, 1),
             "bytes_moved_frac_of_8TBps": round(moved / t_step / 1e6 / HBM_PEAK_GBPS, 4),
+            "bits_per_weight": round(sum(enc[nm].nbytes() for nm in names) * 8 / (weight_bytes / 2), 5),
             "byte_floor_us": round(sum(byte_floor_us(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes)
                                        for nm in names), 2),
             "ms_per_step_with_gate_up_events": round(t_step_instr, 5),
