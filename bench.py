@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--only-layer", action="store_true", help="time only the layer steps (for profiling)")
     ap.add_argument("--only-group", action="store_true",
                     help="time only the grouped layer steps, one w12_gemm_group launch each (for profiling)")
+    ap.add_argument("--summarize-group-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "ALG_BYTES"),
+                    help="turn FETCH_SIZE / WRITE_SIZE rocprofv3 runs of --only-group --copy-probe into the grouped "
+                         "launch's traffic summary under profiles/")
     ap.add_argument("--summarize-group-trace", nargs=3, metavar=("STATS_CSV", "TRACE_CSV", "COMMAND"),
                     help="turn a rocprofv3 --kernel-trace --stats run of --only-group into the grouped-launch "
                          "kernel-time summary under profiles/")
@@ -143,6 +146,9 @@ def main():
         return
     if args.summarize_group_trace:
         summarize_group_trace(*args.summarize_group_trace)
+        return
+    if args.summarize_group_counters:
+        summarize_group_counters(*args.summarize_group_counters)
         return
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
@@ -211,8 +217,15 @@ def main():
             group_only(i)
         t_o = timed(group_only, args.steps, stream)
         moved_o = sum(alg_bytes(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes) for nm in names)
+        if args.copy_probe:
+            a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            torch.cuda.synchronize()
+            torch.bitwise_not(a, out=b)   # one elementwise kernel: reads and writes 256 MiB
+            torch.cuda.synchronize()
         print(json.dumps({"what": "grouped layer step (qkv, o_proj, gate_up, down at M=16, one launch)",
-                          "ms_per_step": round(t_o, 5), "bytes_moved_GBps": round(moved_o / t_o / 1e6, 1)}))
+                          "ms_per_step": round(t_o, 5), "bytes_moved_GBps": round(moved_o / t_o / 1e6, 1),
+                          "alg_bytes_per_launch": int(moved_o)}))
         return
 
     # HIP events bracket every gate_up launch of the roofline pass (same stream as the launch);
@@ -743,6 +756,37 @@ def summarize_group_trace(stats_csv, trace_csv, command):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def summarize_group_counters(fetch_csv, write_csv, alg_bytes_str):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the grouped layer launches, each scaled by the
+    same counter's reading for the 256 MiB torch copy of the same run, against the launch's
+    algorithmic bytes."""
+    copy_bytes = 256 << 20
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _counter_rows(path) if r.get("Counter_Name") == name]
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        grp = [float(r["Counter_Value"]) for r in rows if "k_gemm_group" in r["Kernel_Name"]]
+        probe = [float(r["Counter_Value"]) for r in rows if "elementwise" in r["Kernel_Name"].lower()]
+        if not grp or not probe:
+            raise SystemExit(f"{path}: no grouped GEMM or elementwise probe dispatch found")
+        scale = copy_bytes / (probe[-1] * 1024.0)
+        res[name] = float(np.median(grp)) * 1024 * scale
+    alg = float(alg_bytes_str)
+    out = {"kernel": "w12::k_gemm_group<w12::MfmaPath<1>> (qkv, o_proj, gate_up and down at M=16 in one launch)",
+           "fetch_bytes_per_launch": res["FETCH_SIZE"], "write_bytes_per_launch": res["WRITE_SIZE"],
+           "hbm_bytes_per_launch": res["FETCH_SIZE"] + res["WRITE_SIZE"], "alg_bytes_per_launch": alg,
+           "traffic_over_alg": round((res["FETCH_SIZE"] + res["WRITE_SIZE"]) / alg, 4),
+           "commands": [f"rocprofv3 --pmc {c} -f csv -d gpurun_out/gpmc_{c.split('_')[0].lower()} -o run -- "
+                        "python3 bench.py --only-group --steps 3 --warmup 1 --copy-probe"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "scaling": "each counter is scaled by 256 MiB / (its reading for the probe's elementwise kernel, "
+                      "which reads and writes exactly 256 MiB)"}
+    path = os.path.join(ROOT, "profiles", "gemm_group_layer_M16_counters.txt")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def _counter_rows(path):
