@@ -137,7 +137,17 @@ def main():
                     help="turn a rocprofv3 --pmc run of --mfma-probe (SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and the probe's own output into the "
                          "MFMA summary under profiles/")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="only gate_up at M=1, 8, 16 and 32 (three launches each on rotating copies), for the "
+                         "VALU instruction counters; prints their event times as JSON")
+    ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_CSV", "PROBE_JSON"),
+                    help="turn a rocprofv3 --pmc run of --valu-probe (SQ_WAVES, SQ_INSTS_VALU, SQ_INSTS_MFMA, "
+                         "SQ_INSTS_SALU, SQ_INSTS_LDS, GRBM_GUI_ACTIVE) and the probe's own output into the "
+                         "VALU-budget summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_valu:
+        summarize_valu(*args.summarize_valu)
+        return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
         return
@@ -164,6 +174,9 @@ def main():
     m_step = 16
     if args.mfma_probe:
         mfma_probe(dev, stream)
+        return
+    if args.valu_probe:
+        gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M)
         return
 
     # ---- inputs (synthetic, seeded; host-generated so bits do not depend on the GPU) ----
@@ -450,16 +463,25 @@ MFMA_PROBE_M = (256, 512)
 MFMA_PROBE_MATS = ("gate_up", "down")
 
 
+VALU_PROBE_M = (1, 8, 16, 32)
+VALU_PROBE_MATS = ("gate_up",)
+
+
 def mfma_probe(dev, stream):
-    """gate_up and down at M = 256 and 512 (the batched-verify tiles), three launches each on
-    three rotating encoded copies, in a fixed order; prints the per-launch event times."""
-    layer = S.layer(0, which=MFMA_PROBE_MATS)
+    """gate_up and down at M = 256 and 512 (the batched-verify tiles)."""
+    gemm_probe(dev, stream, MFMA_PROBE_MATS, MFMA_PROBE_M)
+
+
+def gemm_probe(dev, stream, mats, ms):
+    """Layer 0's matrices in ``mats`` at every M of ``ms``, three launches each on three rotating
+    encoded copies, in a fixed order (matrix-major); prints the per-launch event times."""
+    layer = S.layer(0, which=mats)
     res = {}
-    for nm in MFMA_PROBE_MATS:
+    for nm in mats:
         n, k = S.LAYER_SHAPES[nm]
         e0 = w12.encode(dev_bits(layer[nm]))
         cs = [e0, clone_tensor(e0), clone_tensor(e0)]
-        for m in MFMA_PROBE_M:
+        for m in ms:
             x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
             y = torch.empty(m, n, dtype=torch.float32, device=dev)
             ws = w12.gemm_workspace(m, n, k)
@@ -528,6 +550,58 @@ def summarize_mfma(pmc_csv, probe_json):
                 "useful_TFLOPs": round(probe[key]["flops"] / t_us / 1e6, 1),
                 "frac_of_bf16_peak": round(probe[key]["flops"] / t_us / 1e6 / 2500.0, 4)}
     path = os.path.join(ROOT, "profiles", "gemm_M256_M512_mfma_counters.txt")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def summarize_valu(pmc_csv, probe_json):
+    """VALU budget of the streaming GEMM (gate_up at M = 1, 8, 16, 32 from --valu-probe).
+
+    The counters are summed over the GPU per dispatch; each case uses the middle of its three
+    launches and the probe's own event time for it.  A wave64 VALU instruction occupies a 16-lane
+    SIMD for 4 cycles, so the VALU issue floor of a launch is SQ_INSTS_VALU x 4 cycles spread over
+    every SIMD at 2.4 GHz (MFMA instructions are counted apart and excluded from it).  Lane-ops per
+    weight = (SQ_INSTS_VALU - SQ_INSTS_MFMA) x 64 / (N K); the chip issues 1024 SIMDs x 16 lanes x
+    2.4 GHz = 39.3 T lane-ops/s, i.e. 9.2 lane-ops per weight when weights stream at 6.4 TB/s
+    (1.5 bytes each)."""
+    rows = _counter_rows(pmc_csv)
+    by_disp = {}
+    for r in rows:
+        if "k_gemm" not in r["Kernel_Name"]:
+            continue
+        d = by_disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[i] for i in sorted(by_disp)]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    simds, clock = 1024, 2.4e9
+    lane_rate = simds * 16 * clock
+    out = {"commands": [
+        "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS GRBM_GUI_ACTIVE -f csv "
+        "-d gpurun_out/pmc_valu -o run -- python3 bench.py --valu-probe",
+        "python3 bench.py --valu-probe > gpurun_out/valu_probe.json",
+        f"python3 bench.py --summarize-valu {pmc_csv} {probe_json}"],
+        "simds": simds, "clock_GHz": clock / 1e9, "valu_lane_ops_per_s": lane_rate,
+        "budget_lane_ops_per_weight_at_6.4TBps": round(lane_rate / (6.4e12 / 1.5), 2), "launches": {}}
+    i = 0
+    for nm in VALU_PROBE_MATS:
+        n, k = S.LAYER_SHAPES[nm]
+        for m in VALU_PROBE_M:
+            key = f"{nm}_M{m}"
+            ds = disp[i:i + 3]
+            i += 3
+            mid = ds[1]
+            t_us = probe[key]["launch_us"][1]
+            valu = mid["SQ_INSTS_VALU"] - mid["SQ_INSTS_MFMA"]
+            floor_us = valu * 4 / simds / clock * 1e6
+            out["launches"][key] = {
+                "kernel": probe[key]["kernel"], "grid": probe[key]["grid"], "launch_us": t_us,
+                "waves": int(mid["SQ_WAVES"]), "valu_insts": int(valu), "mfma_insts": int(mid["SQ_INSTS_MFMA"]),
+                "salu_insts": int(mid["SQ_INSTS_SALU"]), "lds_insts": int(mid["SQ_INSTS_LDS"]),
+                "valu_lane_ops_per_weight": round(valu * 64 / (n * k), 3),
+                "valu_issue_floor_us": round(floor_us, 2), "valu_floor_over_time": round(floor_us / t_us, 3)}
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M32_valu_counters.txt")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
