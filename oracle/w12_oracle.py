@@ -63,7 +63,7 @@ TOL_EXP = -12                # R8: tolerance 2^-12 * sum |x w|
 
 @dataclass
 class W12Logical:
-    """The logical W12 tensor: what parity is judged on."""
+    """The logical W12 tensor: the form both sides are compared in."""
     n: int
     k: int
     base: np.ndarray      # uint8 [N]      window base exponent field b_n
