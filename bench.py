@@ -912,7 +912,8 @@ def summarize_counters(fetch_csv, write_csv):
 
 def cpu_baseline(layer, enc):
     """The oracle's decode + FP64 GEMM of gate_up at M=16 (the whole matrix), timed 3 times on all
-    host cores, once on one thread; and the oracle's encode of the same matrix, timed once."""
+    host cores, once on one thread; and the oracle's encode and decode-compare (decode, then a
+    bit-for-bit comparison with the BF16 source) of the same matrix, timed once each."""
     from oracle import w12_oracle as O
     w = layer["gate_up"]
     n, k = w.shape
@@ -921,6 +922,11 @@ def cpu_baseline(layer, enc):
     ref = O.encode(w)
     t_enc = time.perf_counter() - t0
     x = S.activations(16, k, S.x_seed(16, k))
+    log("[bench] cpu baseline: oracle decode-compare of gate_up")
+    t0 = time.perf_counter()
+    same = bool(np.array_equal(O.decode(ref), w))
+    t_cmp = time.perf_counter() - t0
+    assert same, "oracle round trip failed"
 
     def run():
         t0 = time.perf_counter()
@@ -948,6 +954,7 @@ def cpu_baseline(layer, enc):
         "sample": f"gate_up {n}x{k}, M=16: oracle decode + FP64 GEMM, median of 3 runs ({t:.2f} s each)",
         "one_thread": None if t1 is None else {"s": round(t1, 3), "GBps": round(2 * n * k / t1 / 1e9, 3)},
         "oracle_encode": {"s": round(t_enc, 3), "GBps": round(2 * n * k / t_enc / 1e9, 3)},
+        "oracle_decode_compare": {"s": round(t_cmp, 3), "GBps": round(2 * n * k / t_cmp / 1e9, 3)},
     }
 
 
