@@ -138,13 +138,20 @@ def main():
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and the probe's own output into the "
                          "MFMA summary under profiles/")
     ap.add_argument("--valu-probe", action="store_true",
-                    help="only gate_up at M=1, 8, 16 and 32 (three launches each on rotating copies), for the "
-                         "VALU instruction counters; prints their event times as JSON")
+                    help="only gate_up at M=1, 8, 16, 32, 48 and 64 (three launches each on rotating copies), for "
+                         "the VALU instruction and stall counters; prints their event times as JSON")
     ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC_CSV", "PROBE_JSON"),
                     help="turn a rocprofv3 --pmc run of --valu-probe (SQ_WAVES, SQ_INSTS_VALU, SQ_INSTS_MFMA, "
                          "SQ_INSTS_SALU, SQ_INSTS_LDS, GRBM_GUI_ACTIVE) and the probe's own output into the "
                          "VALU-budget summary under profiles/")
+    ap.add_argument("--summarize-stalls", nargs=2, metavar=("PMC_CSV", "PROBE_JSON"),
+                    help="turn a rocprofv3 --pmc run of --valu-probe (SQ_WAVES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, "
+                         "SQ_ACTIVE_INST_ANY, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_BUSY_CYCLES, "
+                         "GRBM_GUI_ACTIVE) and the probe's own output into the wave-stall summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_stalls:
+        summarize_stalls(*args.summarize_stalls)
+        return
     if args.summarize_valu:
         summarize_valu(*args.summarize_valu)
         return
@@ -463,7 +470,7 @@ MFMA_PROBE_M = (256, 512)
 MFMA_PROBE_MATS = ("gate_up", "down")
 
 
-VALU_PROBE_M = (1, 8, 16, 32)
+VALU_PROBE_M = (1, 8, 16, 32, 48, 64)
 VALU_PROBE_MATS = ("gate_up",)
 
 
@@ -601,7 +608,56 @@ def summarize_valu(pmc_csv, probe_json):
                 "salu_insts": int(mid["SQ_INSTS_SALU"]), "lds_insts": int(mid["SQ_INSTS_LDS"]),
                 "valu_lane_ops_per_weight": round(valu * 64 / (n * k), 3),
                 "valu_issue_floor_us": round(floor_us, 2), "valu_floor_over_time": round(floor_us / t_us, 3)}
-    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M32_valu_counters.txt")
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M64_valu_counters.txt")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def _probe_dispatches(pmc_csv):
+    rows = _counter_rows(pmc_csv)
+    by_disp = {}
+    for r in rows:
+        if "k_gemm" not in r["Kernel_Name"]:
+            continue
+        d = by_disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [by_disp[i] for i in sorted(by_disp)]
+
+
+def summarize_stalls(pmc_csv, probe_json):
+    """Where the waves of the streaming GEMM spend their time (gate_up at M = 1..64 from
+    --valu-probe; the middle launch of each case).  The kernel's cycles are GRBM_GUI_ACTIVE / XCDs
+    and every wave lives about that long, so wave-cycles = SQ_WAVES x kernel cycles; SQ_WAIT_ANY and
+    SQ_WAIT_INST_ANY count quad-cycles (x 4), SQ_ACTIVE_INST_ANY cycles.  The LDS conflict share is
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    disp = _probe_dispatches(pmc_csv)
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    xcds = 8
+    out = {"commands": [
+        "rocprofv3 --pmc SQ_WAVES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_LDS_BANK_CONFLICT "
+        "SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_stall -o run -- "
+        "python3 bench.py --valu-probe",
+        "python3 bench.py --valu-probe > gpurun_out/valu_probe.json",
+        f"python3 bench.py --summarize-stalls {pmc_csv} {probe_json}"], "launches": {}}
+    i = 0
+    for nm in VALU_PROBE_MATS:
+        for m in VALU_PROBE_M:
+            key = f"{nm}_M{m}"
+            mid = disp[i + 1]
+            i += 3
+            cyc = mid["GRBM_GUI_ACTIVE"] / xcds
+            wave_cycles = mid["SQ_WAVES"] * cyc
+            lds = mid["SQ_LDS_IDX_ACTIVE"]
+            out["launches"][key] = {
+                "kernel": probe[key]["kernel"], "grid": probe[key]["grid"], "launch_us": probe[key]["launch_us"][1],
+                "waves": int(mid["SQ_WAVES"]), "kernel_cycles": int(cyc),
+                "wait_any_frac": round(4 * mid["SQ_WAIT_ANY"] / wave_cycles, 3),
+                "wait_inst_issue_frac": round(4 * mid["SQ_WAIT_INST_ANY"] / wave_cycles, 3),
+                "active_inst_frac": round(mid["SQ_ACTIVE_INST_ANY"] / wave_cycles, 3),
+                "lds_conflict_over_active": round(mid["SQ_LDS_BANK_CONFLICT"] / lds, 3) if lds else None}
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M64_stall_counters.txt")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
