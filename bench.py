@@ -12,7 +12,7 @@ timed steps.  Extra legs (same JSON line): the tree-verify M sweep, per-launch r
 the dominant kernel (gate_up), load-time encode/verify throughput, and the CPU oracle
 timed on the host cores.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50]
 """
 from __future__ import annotations
 
@@ -106,7 +106,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -218,8 +218,9 @@ def main():
             f"encode {t_enc:.3f} ms verify {t_ver:.3f} ms")
     # ---- checkpoint leg: the layer's W12 file streamed back, checked against the BF16 source ----
     out_ckpt = checkpoint_leg(enc, w_dev, names)
+    # the caching allocator keeps this memory: returning it to the driver right before the timed
+    # steps slows the first few hundred launches after it
     del w_dev
-    torch.cuda.empty_cache()
 
     copies = [enc] + [{nm: clone_tensor(enc[nm]) for nm in names} for _ in range(args.copies - 1)]
     y_dev = {nm: torch.empty(m_step, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names}
