@@ -729,7 +729,8 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
         del lay
     bad = int(res[:, :, 0].sum().item())
     assert bad == 0, f"full-model load-time check: {bad} mismatching weights"
-    torch.cuda.empty_cache()
+    # the freed BF16 layers stay in torch's cache: returning memory to the driver right before
+    # the timed passes slows the launches that follow it
     escapes = sum(enc[nm].num_escapes for enc in model for nm in names)
     w12_bytes = sum(enc[nm].nbytes() for enc in model for nm in names)
     log(f"[bench] full model: {n_layers} layers, {w12_bytes / 1e9:.2f} GB W12, encode {t_enc:.1f} ms, "
