@@ -48,8 +48,12 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
           const uint32_t v[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            atomicAdd(&h[(v[j] >> 7) & 0xFFu], 1u);
-            atomicAdd(&h[(v[j] >> 23) & 0xFFu], 1u);
+            // the word's two exponents; when they are equal (about one word in five for
+            // Gaussian weights) one addition of 2 replaces two of 1, so the second addition
+            // runs with fewer lanes on the contended histogram words
+            const uint32_t e0 = (v[j] >> 7) & 0xFFu, e1 = (v[j] >> 23) & 0xFFu;
+            atomicAdd(&h[e0], e0 == e1 ? 2u : 1u);
+            if (e0 != e1) atomicAdd(&h[e1], 1u);
           }
         }
       }
