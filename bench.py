@@ -148,7 +148,13 @@ def main():
                     help="turn a rocprofv3 --pmc run of --valu-probe (SQ_WAVES, SQ_WAIT_ANY, SQ_WAIT_INST_ANY, "
                          "SQ_ACTIVE_INST_ANY, SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE, SQ_BUSY_CYCLES, "
                          "GRBM_GUI_ACTIVE) and the probe's own output into the wave-stall summary under profiles/")
+    ap.add_argument("--summarize-encode-lds", nargs=2, metavar=("PMC_CSV", "FETCH_CSV"),
+                    help="turn two rocprofv3 --pmc runs of --valu-probe (LDS counters; FETCH_SIZE) into the "
+                         "encode-kernel LDS summary under profiles/")
     args = ap.parse_args()
+    if args.summarize_encode_lds:
+        summarize_encode_lds(*args.summarize_encode_lds)
+        return
     if args.summarize_stalls:
         summarize_stalls(*args.summarize_stalls)
         return
@@ -662,6 +668,46 @@ def summarize_stalls(pmc_csv, probe_json):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def summarize_encode_lds(pmc_csv, fetch_csv):
+    """LDS use of the encode kernels on gate_up (the --valu-probe run encodes it once: count, scan,
+    emit).  Kernel cycles = GRBM_GUI_ACTIVE / 8 XCDs; the LDS-busy share is SQ_LDS_IDX_ACTIVE /
+    (256 CUs x kernel cycles); FETCH_SIZE is scaled by the copy-probe factor of the layer-step
+    traffic runs (2.00)."""
+    def by_kernel(path):
+        agg = {}
+        for r in _counter_rows(path):
+            for kn in ("k_encode_count", "k_encode_emit_blocks", "k_encode_emit_rows"):
+                if kn in r["Kernel_Name"]:
+                    d = agg.setdefault(kn, {})
+                    d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return agg
+    a, f = by_kernel(pmc_csv), by_kernel(fetch_csv)
+    cmds = [
+        "rocprofv3 --pmc SQ_WAVES SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_INSTS_VALU "
+        "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d gpurun_out/pmc_cnt -o run -- python3 bench.py --valu-probe",
+        "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_cnt2 -o run -- python3 bench.py --valu-probe",
+        f"python3 bench.py --summarize-encode-lds {pmc_csv} {fetch_csv}"]
+    lines = ["# LDS counters of the encode kernels (gate_up 34816 x 5120), MI355X", "",
+             "Commands (run from the repository root):", "", "```"] + cmds + ["```", "",
+             "The probe encodes gate_up once. Counters are summed over the GPU. Kernel cycles = GRBM_GUI_ACTIVE / 8",
+             "XCDs; the LDS-busy share is SQ_LDS_IDX_ACTIVE / (256 CUs x kernel cycles). FETCH_SIZE is scaled by the",
+             "copy-probe factor of the layer-step traffic runs (2.00).", "",
+             "| kernel | waves | kernel cycles | LDS instructions per wave | LDS busy share per CU | "
+             "conflict cycles / LDS-active cycles | VALU instructions per wave | HBM fetch (MB) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for kn, c in a.items():
+        cyc = c["GRBM_GUI_ACTIVE"] / 8
+        lines.append(f"| `{kn}` | {int(c['SQ_WAVES'])} | {int(cyc)} | {c['SQ_INSTS_LDS'] / c['SQ_WAVES']:.0f} | "
+                     f"{c['SQ_LDS_IDX_ACTIVE'] / (256 * cyc):.3f} | "
+                     f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.3f} | "
+                     f"{c['SQ_INSTS_VALU'] / c['SQ_WAVES']:.0f} | "
+                     f"{f.get(kn, {}).get('FETCH_SIZE', 0.0) * 1024 * 2.0 / 1e6:.1f} |")
+    path = os.path.join(ROOT, "profiles", "encode_gate_up_lds_counters.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def checkpoint_leg(enc, w_dev, names, reps=3):
