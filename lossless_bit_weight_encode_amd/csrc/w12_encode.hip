@@ -102,45 +102,66 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
 }
 
 // esc_ptr[0] = 0 and an inclusive scan of the counts in esc_ptr[1..N] (one work-group).
-// Thread t owns the contiguous stretch [1 + t per, 1 + (t+1) per); it loads its counts
-// kScanBatch at a time with every load of a batch issued before any is used (for N up to
-// 49152 the whole stretch is one batch and stays in registers between the two passes).
+// The counts stream through LDS in chunks of kScanChunk: coalesced loads into LDS; each thread
+// sums and then scans its kScanPer contiguous counts there (one pad word every 32 keeps those
+// strided reads to 2-way bank conflicts); wave shuffles and one pass over the wave totals give
+// each thread its offset; coalesced stores write the chunk back, and the chunk's total carries
+// into the next one.
 constexpr int kScanThreads = 1024;
-constexpr int kScanBatch = 48;
+constexpr int kScanPer = 16;
+constexpr int kScanChunk = kScanThreads * kScanPer;
+constexpr int kScanWaves = kScanThreads / kWave;
+__device__ __forceinline__ int scan_slot(int i) { return i + (i >> 5); }
 __global__ __launch_bounds__(kScanThreads) void k_scan_counts(uint32_t* __restrict__ esc_ptr, int32_t N) {
-  __shared__ uint32_t part[kScanThreads];
-  const int t = threadIdx.x;
-  const int64_t per = ((int64_t)N + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = 1 + (int64_t)t * per;
-  const int64_t hi = (lo + per < (int64_t)N + 1) ? lo + per : (int64_t)N + 1;
-  uint32_t v[kScanBatch];
-  uint32_t s = 0;
-  for (int64_t i0 = lo; i0 < hi; i0 += kScanBatch) {
+  __shared__ uint32_t buf[kScanChunk + kScanChunk / 32];
+  __shared__ uint32_t wtot[kScanWaves];
+  const int t = threadIdx.x, lane = t & (kWave - 1), wave = t / kWave;
+  uint32_t carry = 0;   // the counts of the earlier chunks
+  for (int64_t c0 = 1; c0 <= (int64_t)N; c0 += kScanChunk) {
+    const int len = (int)((int64_t)N + 1 - c0 < kScanChunk ? (int64_t)N + 1 - c0 : kScanChunk);
 #pragma unroll
-    for (int k = 0; k < kScanBatch; ++k) v[k] = (i0 + k < hi) ? esc_ptr[i0 + k] : 0u;
-#pragma unroll
-    for (int k = 0; k < kScanBatch; ++k) s += v[k];
-  }
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const uint32_t x = (t >= off) ? part[t - off] : 0u;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
-  uint32_t run = (t > 0) ? part[t - 1] : 0u;
-  const bool one_batch = per <= kScanBatch;   // v still holds the stretch
-  for (int64_t i0 = lo; i0 < hi; i0 += kScanBatch) {
-    if (!one_batch) {
-#pragma unroll
-      for (int k = 0; k < kScanBatch; ++k) v[k] = (i0 + k < hi) ? esc_ptr[i0 + k] : 0u;
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = k * kScanThreads + t;
+      uint32_t x = 0;
+      if (i < len) x = esc_ptr[c0 + i];
+      buf[scan_slot(i)] = x;
     }
+    __syncthreads();
+    uint32_t v[kScanPer];
+    uint32_t s = 0;
 #pragma unroll
-    for (int k = 0; k < kScanBatch; ++k) {
-      run += v[k];
-      if (i0 + k < hi) esc_ptr[i0 + k] = run;
+    for (int j = 0; j < kScanPer; ++j) {
+      v[j] = buf[scan_slot(t * kScanPer + j)];
+      s += v[j];
     }
+    uint32_t inc = s;   // inclusive scan of the thread sums within the wave
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t o = __shfl_up(inc, off, kWave);
+      if (lane >= off) inc += o;
+    }
+    if (lane == kWave - 1) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t run = carry + (inc - s), total = 0;
+    for (int w = 0; w < kScanWaves; ++w) {
+      const uint32_t x = wtot[w];
+      run += w < wave ? x : 0u;
+      total += x;
+    }
+    // each thread rewrites only the slots it read
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      run += v[j];
+      buf[scan_slot(t * kScanPer + j)] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      const int i = k * kScanThreads + t;
+      if (i < len) esc_ptr[c0 + i] = buf[scan_slot(i)];
+    }
+    carry += total;
+    __syncthreads();   // buf and wtot are rewritten by the next chunk
   }
   if (t == 0) esc_ptr[0] = 0;
 }
