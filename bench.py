@@ -208,9 +208,10 @@ def main():
     for nm in names:
         w = w_dev[nm]
         n, k = w.shape
+        enc[nm] = w12.encode(w)   # untimed: the first launch of each kernel loads its code
         t_enc = timed(lambda i: w12.encode(w), 3, stream)
-        enc[nm] = w12.encode(w)
         res = torch.empty(2, dtype=torch.int64, device=dev)
+        w12.verify_async(enc[nm], w, res)
         t_ver = timed(lambda i: w12.verify_async(enc[nm], w, res), 5, stream)
         cnt, first = res.cpu().tolist()
         assert cnt == 0, f"load-time check failed on {nm}: {cnt} mismatches (first {first})"
