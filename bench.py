@@ -151,7 +151,15 @@ def main():
     ap.add_argument("--summarize-encode-lds", nargs=2, metavar=("PMC_CSV", "FETCH_CSV"),
                     help="turn two rocprofv3 --pmc runs of --valu-probe (LDS counters; FETCH_SIZE) into the "
                          "encode-kernel LDS summary under profiles/")
+    ap.add_argument("--probe-reps", type=int, default=3,
+                    help="launches per case of --valu-probe (the counter summaries expect 3)")
+    ap.add_argument("--summarize-sweep-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace run of --valu-probe into the per-M kernel-time summary "
+                         "under profiles/")
     args = ap.parse_args()
+    if args.summarize_sweep_trace:
+        summarize_sweep_trace(*args.summarize_sweep_trace)
+        return
     if args.summarize_encode_lds:
         summarize_encode_lds(*args.summarize_encode_lds)
         return
@@ -189,7 +197,7 @@ def main():
         mfma_probe(dev, stream)
         return
     if args.valu_probe:
-        gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M)
+        gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M, args.probe_reps)
         return
 
     # ---- inputs (synthetic, seeded; host-generated so bits do not depend on the GPU) ----
@@ -487,8 +495,8 @@ def mfma_probe(dev, stream):
     gemm_probe(dev, stream, MFMA_PROBE_MATS, MFMA_PROBE_M)
 
 
-def gemm_probe(dev, stream, mats, ms):
-    """Layer 0's matrices in ``mats`` at every M of ``ms``, three launches each on three rotating
+def gemm_probe(dev, stream, mats, ms, reps=3):
+    """Layer 0's matrices in ``mats`` at every M of ``ms``, ``reps`` launches each on three rotating
     encoded copies, in a fixed order (matrix-major); prints the per-launch event times."""
     layer = S.layer(0, which=mats)
     res = {}
@@ -500,16 +508,17 @@ def gemm_probe(dev, stream, mats, ms):
             x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
             y = torch.empty(m, n, dtype=torch.float32, device=dev)
             ws = w12.gemm_workspace(m, n, k)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for i, (a, b) in enumerate(evs):
                 a.record(stream)
-                w12.gemm(x, cs[i], y=y, ws=ws, stream=stream)
+                w12.gemm(x, cs[i % len(cs)], y=y, ws=ws, stream=stream)
                 b.record(stream)
             torch.cuda.synchronize()
             plan = w12.gemm_plan(m, n, k)
             res[f"{nm}_M{m}"] = {"kernel": kernel_name(plan, m), "launch_us": [round(a.elapsed_time(b) * 1e3, 2)
                                                                               for a, b in evs],
-                                 "flops": 2 * m * n * k, "grid": plan["grid"], "m_tile": plan["m_tile"]}
+                                 "flops": 2 * m * n * k, "grid": plan["grid"], "m_tile": plan["m_tile"],
+                                 "escapes": e0.num_escapes}
         del cs, e0
         torch.cuda.empty_cache()
     print(json.dumps(res))
@@ -669,6 +678,43 @@ def summarize_stalls(pmc_csv, probe_json):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def summarize_sweep_trace(trace_csv, probe_json, command):
+    """rocprofv3 kernel durations of the --valu-probe GEMM launches (gate_up at M = 1..64, in probe
+    order, R launches per M), the first launch of each M dropped; weight-GB/s = 2NK / t and the
+    fraction of 8 TB/s from the algorithmic bytes of each M."""
+    import csv
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    gemm = [r for r in trace if "k_gemm" in r["Kernel_Name"]]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    lines = ["# W12 GEMM kernel times over the M sweep: gate_up 34816 x 5120, MI355X", "",
+             "Command (run from the repository root):", "", "```", command, "```", "",
+             "Kernel trace durations; each M runs R launches on three rotating encoded copies (the first is "
+             "dropped).", "Moved bytes are the algorithmic bytes of the launch (records, bases, pointers, "
+             "escapes, X, Y).", "",
+             "| M | kernel | launches | avg us | median us | min us | weight-GB/s (median) | "
+             "moved GB/s (median) | of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for nm in VALU_PROBE_MATS:
+        n, k = S.LAYER_SHAPES[nm]
+        for m in VALU_PROBE_M:
+            info = probe[f"{nm}_M{m}"]
+            reps = len(info["launch_us"])
+            rows = gemm[i:i + reps][1:]
+            i += reps
+            d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
+            med = float(np.median(d))
+            moved = alg_bytes(n, k, m, info["escapes"])
+            lines.append(f"| {m} | `{info['kernel']}` | {len(d)} | {d.mean():.2f} | {med:.2f} | {d.min():.2f} | "
+                         f"{2 * n * k / med / 1e3:.0f} | {moved / med / 1e3:.0f} | "
+                         f"{moved / med / 1e3 / HBM_PEAK_GBPS:.3f} |")
+    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M64_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_encode_lds(pmc_csv, fetch_csv):
