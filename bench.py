@@ -91,6 +91,40 @@ def timed_blocks(fn, iters, stream, blocks=5):
     return ev[0].elapsed_time(ev[nb]) / iters, per
 
 
+READ_SIZES = {"o_proj_39MB": 39_340_032, "down_134MB": 133_693_440, "gate_up_267MB": 267_386_880,
+              "1GiB": 1 << 30}
+# the read-probe shape the default run reports (the fastest of the --read-probe sweep)
+READ_BEST = (8, 2)   # (loads in flight per lane, 256-thread work-groups per CU)
+
+
+def read_ceiling(dev, stream, variants, sizes=READ_SIZES, reps=20):
+    """Plain streaming reads (w12_read_probe) of each size, rotating over a 2 GiB buffer so the
+    256 MB Infinity Cache cannot serve a repeat; per-launch HIP events on the launch stream.
+    Returns {size: {"U<u>_G<g>": {"us": median, "GBps": bytes / median}}}."""
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(16 * 1024, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nb in sizes.items():
+        nb = nb // 256 * 256
+        slots = max(1, (buf.numel() - nb) // nb + 1)
+        res = {}
+        for u, g in variants:
+            for i in range(3):
+                w12.read_probe(buf, nb, u, g, sink, offset=(i % slots) * nb, stream=stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            torch.cuda.synchronize()
+            for i in range(reps):
+                ev[i][0].record(stream)
+                w12.read_probe(buf, nb, u, g, sink, offset=((i + 3) % slots) * nb, stream=stream)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+            res[f"U{u}_G{g}"] = {"us": round(us, 2), "GBps": round(nb / us / 1e3, 1)}
+        out[name] = res
+    del buf, sink
+    return out
+
+
 def ci95(samples):
     """Median and the half-width of a t-based 95% confidence interval of the mean."""
     import statistics
@@ -151,6 +185,8 @@ def main():
     ap.add_argument("--summarize-encode-lds", nargs=2, metavar=("PMC_CSV", "FETCH_CSV"),
                     help="turn two rocprofv3 --pmc runs of --valu-probe (LDS counters; FETCH_SIZE) into the "
                          "encode-kernel LDS summary under profiles/")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="sweep the plain streaming-read kernel (loads in flight x work-groups per CU) and exit")
     ap.add_argument("--probe-reps", type=int, default=3,
                     help="launches per case of --valu-probe (the counter summaries expect 3)")
     ap.add_argument("--summarize-sweep-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
@@ -198,6 +234,15 @@ def main():
         return
     if args.valu_probe:
         gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M, args.probe_reps)
+        return
+    if args.read_probe:
+        variants = [(u, g) for u in (1, 2, 4, 8, 16) for g in (1, 2, 4, 8)]
+        res = read_ceiling(dev, stream, variants)
+        for nm, r in res.items():
+            best = max(r, key=lambda v: r[v]["GBps"])
+            log(f"[read] {nm}: best {best} {r[best]['GBps']} GB/s")
+        print(json.dumps({"what": "plain streaming read (w12_read_probe), median of per-launch events",
+                          "read": res}))
         return
 
     # ---- inputs (synthetic, seeded; host-generated so bits do not depend on the GPU) ----
@@ -468,12 +513,20 @@ def main():
         torch.cuda.empty_cache()
         out["full_model"] = full_model_leg(dev, stream, args.model_layers, 32)
 
-    # ---- practical HBM ceilings measured with plain torch kernels (context for frac) ----
+    # ---- practical HBM ceilings (context for frac): the hand-written streaming read at the
+    # matrices' sizes, and a plain torch copy ----
+    rd = read_ceiling(dev, stream, [READ_BEST])
+    key = f"U{READ_BEST[0]}_G{READ_BEST[1]}"
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     bcp = torch.empty_like(a)
     t_cp = timed(lambda i: bcp.copy_(a), 10, stream)
-    out["hbm_reference"] = {"copy_1GiB_GBps": round(2 * a.numel() / t_cp / 1e6, 1)}
-    log(f"[bench] plain copy {2 * a.numel() / t_cp / 1e6:.0f} GB/s")
+    out["hbm_reference"] = {
+        "what": "w12_read_probe: plain streaming read, %d loads in flight per lane, %d work-groups per CU; "
+                "median of 20 launches rotating over 2 GiB" % READ_BEST,
+        "read_GBps": {nm: r[key]["GBps"] for nm, r in rd.items()},
+        "read_us": {nm: r[key]["us"] for nm, r in rd.items()},
+        "copy_1GiB_GBps": round(2 * a.numel() / t_cp / 1e6, 1)}
+    log(f"[bench] plain read {out['hbm_reference']['read_GBps']} GB/s, copy {2 * a.numel() / t_cp / 1e6:.0f} GB/s")
     del a, bcp
 
     # ---- CPU oracle on the host cores (a reported baseline, not the target) ----

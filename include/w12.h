@@ -128,10 +128,10 @@ int w12_verify(const w12_tensor *t, const uint16_t *ref, int64_t ldr,
 int w12_unpack_records(const w12_tensor *t, uint16_t *rec, int64_t ldr, hipStream_t stream);
 
 /* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only.
- * The workspace starts with one 32-bit arrival counter per output tile (split-K
- * bookkeeping) followed by the FP32 slice partials.  The size follows the plan, so a change
- * of W12_GEMV_MAX_M between sizing and calling can make the workspace too small (reported as
- * W12_ERR_WORKSPACE_TOO_SMALL). */
+ * The workspace starts with a 16 KB region of 32-bit arrival counters (split-K bookkeeping;
+ * the same region for every plan, single or grouped) followed by the FP32 slice partials.
+ * The size follows the plan, so a change of W12_GEMV_MAX_M between sizing and calling can
+ * make the workspace too small (reported as W12_ERR_WORKSPACE_TOO_SMALL). */
 int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
 
 /* Zero-fill a GEMM workspace of ws_bytes bytes on `stream`.  Call it once after allocating
@@ -202,13 +202,14 @@ int w12_gemm_group_q(int32_t M, int32_t count, const w12_gemm_item *items, void 
 
 /* How w12_gemm will run (M, N, K).  Host only. */
 typedef struct w12_gemm_plan_info {
-  int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles                       */
+  int32_t path;              /* 1 = wavefront GEMV, 2 = MFMA tiles, 3 = wide MFMA tiles  */
   int32_t splits;            /* most K slices (partial sums) of one output tile          */
   int32_t rows_per_block;    /* rows of W per work-group tile                            */
   int32_t m_tile;            /* rows of X per work-group tile                            */
   int64_t grid;              /* work-groups launched                                     */
   uint64_t workspace_bytes;  /* == w12_gemm_workspace_size                               */
-  uint64_t counter_bytes;    /* leading bytes of the workspace holding arrival counters */
+  uint64_t counter_bytes;    /* leading bytes of the workspace holding the counters (the
+                                same for every plan)                                      */
 } w12_gemm_plan_info;
 int w12_gemm_plan(int32_t M, int32_t N, int32_t K, w12_gemm_plan_info *info);
 
@@ -254,6 +255,19 @@ int w12_file_index(const char *path, int32_t *count, w12_file_entry *entries, in
 int w12_file_load(const char *path, int32_t count, const int32_t *which, const w12_tensor *dst,
                   void *staging, uint64_t staging_bytes, const uint16_t *const *refs, const int64_t *ldr,
                   unsigned long long *d_results, hipStream_t stream);
+
+/*
+ * Measurement aid (not part of the format): a plain streaming read of buf[0, bytes) by
+ * groups_per_cu 256-thread work-groups per compute unit, each reading a contiguous share with
+ * 16-byte loads (1 KB of consecutive bytes per wave instruction) and keeping loads_per_lane
+ * (1, 2, 4, 8 or 16) loads in flight per lane.  It gives the practical HBM read ceiling that the
+ * GEMM's bytes moved per second are compared with.  buf: device, 16-byte aligned; bytes: a
+ * multiple of 16, 16 <= bytes <= 2^31; groups_per_cu: 1..16; sink: device, at least
+ * groups_per_cu * (compute units) uint32 values, never written in practice (the loaded data
+ * is folded into a value that is stored only if it equals a fixed constant).
+ */
+int w12_read_probe(const void *buf, uint64_t bytes, int32_t loads_per_lane, int32_t groups_per_cu,
+                   uint32_t *sink, hipStream_t stream);
 
 /* Stored bits per weight: (1.5*N*K + N + 4*(N+1) + 4*E) * 8 / (N*K). */
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E);

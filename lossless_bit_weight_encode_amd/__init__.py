@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     layout_bytes,
     lib,
     load,
+    read_probe,
     save,
     unpack_records,
     verify,

@@ -67,6 +67,7 @@ _SIGNATURES = {
     "w12_file_index": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_c_i32), ctypes.POINTER(_FileEntry), _c_i32]),
     "w12_file_load": (ctypes.c_int, [ctypes.c_char_p, _c_i32, ctypes.POINTER(_c_i32), ctypes.POINTER(_Tensor), _c_p,
                                      _c_u64, ctypes.POINTER(_c_p), ctypes.POINTER(_c_i64), _c_p, _c_p]),
+    "w12_read_probe": (ctypes.c_int, [_c_p, _c_u64, _c_i32, _c_i32, _c_p, _c_p]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
     "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w12_last_error": (ctypes.c_char_p, []),
@@ -295,6 +296,17 @@ def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch
     _check(name, getattr(lib(), name)(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
                                       _stream(stream)))
     return y
+
+
+def read_probe(buf: torch.Tensor, nbytes: int, loads_per_lane: int, groups_per_cu: int, sink: torch.Tensor,
+               offset: int = 0, stream=None) -> None:
+    """A plain streaming read of nbytes bytes of buf starting at byte offset (w12_read_probe): the
+    practical HBM read ceiling.  sink: a device buffer of at least groups_per_cu * CUs uint32."""
+    _require_cuda(buf, sink)
+    if offset < 0 or offset + nbytes > buf.numel() * buf.element_size():
+        raise ValueError("read range outside the buffer")
+    _check("w12_read_probe", lib().w12_read_probe(buf.data_ptr() + offset, nbytes, loads_per_lane, groups_per_cu,
+                                                   _ptr(sink), _stream(stream)))
 
 
 def bits_per_weight(n: int, k: int, e: int) -> float:

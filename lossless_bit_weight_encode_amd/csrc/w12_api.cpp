@@ -6,6 +6,7 @@
 #include <vector>
 
 #include "w12_device.h"
+#include "w12_gemm_common.h"
 #include "w12_kernels.h"
 
 namespace {
@@ -321,6 +322,21 @@ int w12_file_load(const char* path, int32_t count, const int32_t* which, const w
   if (rc == -1) return fail(W12_ERR_IO, "%s", err);
   if (rc) return fail(W12_ERR_HIP, "%s", err);
   return ok();
+}
+
+int w12_read_probe(const void* buf, uint64_t bytes, int32_t loads_per_lane, int32_t groups_per_cu, uint32_t* sink,
+                   hipStream_t stream) {
+  if (!buf || !sink) return fail(W12_ERR_INVALID_ARG, "buf or sink is NULL");
+  // the kernel marks loads past a work-group's share with offset 2^31, which must stay past the buffer
+  if (bytes < 16 || bytes % 16 || bytes > (uint64_t(1) << 31))
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "bytes=%llu must be a multiple of 16 in 16..2^31", (unsigned long long)bytes);
+  if (loads_per_lane != 1 && loads_per_lane != 2 && loads_per_lane != 4 && loads_per_lane != 8 && loads_per_lane != 16)
+    return fail(W12_ERR_INVALID_ARG, "loads_per_lane=%d is not 1, 2, 4, 8 or 16", loads_per_lane);
+  if (groups_per_cu < 1 || groups_per_cu > 16) return fail(W12_ERR_INVALID_ARG, "groups_per_cu=%d outside 1..16", groups_per_cu);
+  if (!aligned(buf, 16)) return fail(W12_ERR_MISALIGNED, "buf must be 16-byte aligned");
+  if (!aligned(sink, 4)) return fail(W12_ERR_MISALIGNED, "sink must be 4-byte aligned");
+  const int64_t grid = (int64_t)w12::device_cus() * groups_per_cu;
+  return hip_status(w12::launch_read_probe(buf, bytes, loads_per_lane, grid, sink, stream), "read_probe");
 }
 
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {

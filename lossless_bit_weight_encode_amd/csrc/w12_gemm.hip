@@ -62,7 +62,7 @@ struct GemmArgs {
   uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
-  uint32_t* counters;   // [tiles] arrival counters of this product's tiles
+  uint32_t* counters;   // [kMaxGrid] arrival counters, indexed by a split tile's first work-group
   float* P;             // [2G][tile elements] partial tiles (shared by a group)
 };
 
@@ -798,9 +798,10 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[threadIdx.x] : 0];
       const int64_t tile = s_pend[threadIdx.x];
       const int64_t t0 = gt.ubase + tile * gt.upt;
-      const uint32_t nsegs =
-          (uint32_t)(ceil_div((t0 + gt.upt) * gt.G, gt.units) - ceil_div((t0 + 1) * gt.G, gt.units) + 1);
-      const uint32_t prev = __hip_atomic_fetch_add(gt.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int64_t w_a = ceil_div((t0 + 1) * gt.G, gt.units) - 1;
+      const uint32_t nsegs = (uint32_t)(ceil_div((t0 + gt.upt) * gt.G, gt.units) - w_a);
+      // a split tile is the last segment of its first work-group w_a, so w_a names its counter
+      const uint32_t prev = __hip_atomic_fetch_add(gt.counters + w_a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
     }
     __syncthreads();
@@ -854,7 +855,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
           if (n < gt.N && m < gt.M) gt.Y[(int64_t)m * gt.ldy + n] = v[k];
         }
       }
-      if (threadIdx.x == 0) __hip_atomic_store(gt.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (threadIdx.x == 0) __hip_atomic_store(gt.counters + w_a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -1140,6 +1141,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", gpc);
   const int max_grid = env_int("W12_MAX_GRID", 0);   // 0: no cap
   if (max_grid > 0 && G > max_grid) G = max_grid;
+  if (G > kMaxGrid) G = kMaxGrid;
   if (G > p.units) G = p.units;
   if (G < 1) G = 1;
   // When the tiles fit in the resident work-groups, use a whole multiple of them (keeping at
@@ -1165,7 +1167,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
     p.splits = (int)best;
   }
   const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
-  p.counter_bytes = ((uint64_t)p.tiles * 4 + 255) / 256 * 256;
+  p.counter_bytes = kCounterBytes;
   p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
   // ragged K: room for X padded to whole chunks
   p.xpad_bytes = (K % kChunkK) ? ((uint64_t)M * (uint64_t)Kc * kChunkK * 2 + 255) / 256 * 256 : 0;
@@ -1312,6 +1314,7 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
   int64_t G = (int64_t)device_cus() * env_int("W12_GROUPS_PER_CU", groups_per_cu<true>(p.path, M, p.m_tile));
   const int max_grid = env_int("W12_MAX_GRID", 0);
   if (max_grid > 0 && G > max_grid) G = max_grid;
+  if (G > kMaxGrid) G = kMaxGrid;
   if (G > p.units) G = p.units;
   if (G < 1) G = 1;
   p.grid = G;
@@ -1335,7 +1338,7 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
     p.splits = (int)best;
   }
   const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
-  p.counter_bytes = ((uint64_t)p.tiles * 4 + 255) / 256 * 256;
+  p.counter_bytes = kCounterBytes;
   p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
   p.xpad_bytes = 0;
   p.ws_bytes = p.counter_bytes + p.partial_bytes;
@@ -1345,7 +1348,7 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
 hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const w12_gemm_item* items,
                              const int64_t* tiles_of, const int64_t* upt_of, void* ws, bool qpass, hipStream_t stream) {
   GroupArgs<kGroupMax> ga{};
-  int64_t ubase = 0, tbase = 0;
+  int64_t ubase = 0;
   for (int i = 0; i < count; ++i) {
     GemmArgs& a = ga.g[i];
     fill_args(a, p, items[i].X, M, items[i].ldx, items[i].t, items[i].Y, items[i].ldy, ws);
@@ -1353,9 +1356,8 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
     a.tiles = tiles_of[i];
     a.upt = upt_of[i];
     a.units = p.units;
-    a.counters = reinterpret_cast<uint32_t*>(ws) + tbase;
+    a.counters = reinterpret_cast<uint32_t*>(ws);
     ubase += tiles_of[i] * upt_of[i];
-    tbase += tiles_of[i];
   }
   for (int i = count; i < kGroupMax; ++i) ga.g[i] = ga.g[0];   // never selected (count bounds gemm_of)
   ga.count = count;

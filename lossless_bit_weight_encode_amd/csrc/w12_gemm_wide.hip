@@ -62,7 +62,7 @@ struct WideArgs {
   uint32_t hi_bytes, lo_bytes, x_bytes, esc_bytes, y_bytes, p_bytes;
   float* Y;
   int64_t ldy;
-  uint32_t* counters;   // [tiles] arrival counters
+  uint32_t* counters;   // [G] arrival counters, indexed by a split tile's first work-group
   float* P;             // [2G][tile elements] partial tiles
 };
 
@@ -416,7 +416,8 @@ void k_gemm_wide(WideArgs g) {
       const int64_t w_b = ceil_div((t0 + g.upt) * g.G, g.units) - 1;
       const int64_t ns = w_b - w_a + 1;
       if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(g.counters + s.tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the tile's counter is its first work-group's (the tile is w_a's last segment)
+        const uint32_t prev = __hip_atomic_fetch_add(g.counters + w_a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(ns - 1)) ? 1u : 0u;
       }
       __syncthreads();
@@ -454,7 +455,7 @@ void k_gemm_wide(WideArgs g) {
             }
           }
         }
-        if (threadIdx.x == 0) __hip_atomic_store(g.counters + s.tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(g.counters + w_a, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     u = s.seg_end;

@@ -18,6 +18,12 @@ hipError_t launch_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, 
                          hipStream_t stream);
 hipError_t launch_unpack(const w12_tensor* t, uint16_t* rec, int64_t ldr, hipStream_t stream);
 
+// Every GEMM workspace starts with the same counter region, whatever the plan, so one
+// initialised workspace serves any sequence of products: one arrival counter per work-group
+// (a split tile counts on its first work-group's), and no launch has more work-groups.
+constexpr int64_t kMaxGrid = 4096;
+constexpr uint64_t kCounterBytes = (uint64_t)kMaxGrid * 4;
+
 struct GemmPlan {
   int path;            // 1 = wavefront GEMV, 2 = MFMA tiles (streaming), 3 = wide MFMA tiles
   int splits;          // partial sums per tile (1 when a tile is never split)
@@ -30,7 +36,7 @@ struct GemmPlan {
   int64_t upt;         // stream-K units (16 chunks) per tile
   int64_t units;       // tiles * upt
   int64_t grid;        // work-groups G (resident at once); w takes units [w U / G, (w+1) U / G)
-  uint64_t counter_bytes;  // per-tile arrival counters at the start of the workspace
+  uint64_t counter_bytes;  // kCounterBytes: the counter region at the start of the workspace
   uint64_t partial_bytes;  // two partial tiles per work-group
   uint64_t xpad_bytes;     // X padded to whole 16-k chunks (only when K % 16 != 0)
   uint64_t ws_bytes;       // counters + partials + padded X
@@ -56,6 +62,10 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
 // qpass: the Q pass on the nested 8-bit view (hi plane only, escapes exact)
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream);
+
+// Measurement aid: a plain streaming read of `bytes` bytes (w12_probe.hip).
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, int32_t loads_per_lane, int64_t grid, uint32_t* sink,
+                             hipStream_t stream);
 
 // Checkpoint files (host side; w12_file.cpp).  Return 0, -1 for an I/O or format error, -2
 // for a HIP error, with a message in err.

@@ -34,6 +34,11 @@ MEMBERS = {
 _cache = {}
 
 
+def counter_bytes():
+    """The counter region at the start of every GEMM workspace (the same for every plan)."""
+    return w12.gemm_plan(1, 16, 16)["counter_bytes"]
+
+
 def member(name):
     if name not in _cache:
         w = MEMBERS[name]()
@@ -57,9 +62,8 @@ def run_group(names, m, seed, qpass=False, repeats=2):
         torch.cuda.synchronize()
         for a, b in zip(ys, ys2):
             assert torch.equal(a, b), "grouped GEMM output is not bitwise repeatable"
-    # every call leaves the arrival counters (one per 64-channel tile, at the start) zero
-    tiles = sum(-(-(-(-t.n // 16)) // 4) for t in ts)
-    assert int(ws[:4 * tiles].count_nonzero()) == 0
+    # every call leaves the arrival counters (a region of the same size for every plan) zero
+    assert int(ws[:counter_bytes()].count_nonzero()) == 0
     for i, nm in enumerate(names):
         yh = ys[i].cpu().numpy()
         if qpass:
@@ -177,7 +181,7 @@ def test_group_deterministic_poisoned_workspace_and_canaries(monkeypatch, m):
     bufs = [torch.full((m + 3, t.n + 11), canary, dtype=torch.float32, device="cuda") for t in ts]
     ys = [b[:m, :t.n] for b, t in zip(bufs, ts)]
     ws = w12.gemm_group_workspace(m, ts)
-    cb = (4 * sum(-(-(-(-t.n // 16)) // 4) for t in ts) + 255) // 256 * 256
+    cb = counter_bytes()
     outs = []
     for _ in range(20):
         ws[cb:].view(torch.uint8).fill_(0xFF)   # NaN patterns in every partial slot
@@ -194,3 +198,39 @@ def test_group_deterministic_poisoned_workspace_and_canaries(monkeypatch, m):
         assert (bh[m:, :] == np.float32(canary)).all(), f"item {i}: write past M"
         bad, worst = O.gemm_check(xs[i], ws_[i], outs[0][i].view(np.float32))
         assert bad == 0, f"item {i}: {bad} outputs outside tolerance"
+
+
+def test_workspace_reused_across_plans():
+    """One workspace serves products whose plans differ (wide tiles, MFMA tiles, the wavefront
+    GEMV, a grouped launch, then wide tiles again): the counter region is the same for every
+    plan, so partial sums of one plan never land where another reads its counters.  Every
+    output is checked against the oracle and the counters are zero after every call."""
+    w, t, _ = member("gauss_300x4096")
+    names = ALL[:4]
+    gts = [member(nm)[1] for nm in names]
+    need = max([w12.gemm_workspace_size(m, t.n, t.k) for m in (1, 16, 256)] +
+               [w12.gemm_group_workspace_size(16, gts)])
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    w12.gemm_workspace_init(ws)
+    cb = counter_bytes()
+    plans = []
+    for step, m in enumerate([256, 16, "group", 1, 256, 33]):
+        say(f"[reuse] step {step} M={m}")
+        if m == "group":
+            xs = [S.activations(16, member(nm)[0].shape[1], 500 + i) for i, nm in enumerate(names)]
+            ys = w12.gemm_group([to_dev(x) for x in xs], gts, ws=ws)
+            torch.cuda.synchronize()
+            for i, nm in enumerate(names):
+                bad, worst = O.gemm_check(xs[i], member(nm)[0], ys[i].cpu().numpy())
+                assert bad == 0, f"group item {nm}: {bad} outputs outside tolerance (worst rel {worst:.3g})"
+        else:
+            plans.append(w12.gemm_plan(m, t.n, t.k)["path"])
+            # partial slots of the previous plan hold stale sums; poison them too
+            ws[cb:].fill_(0xFF)
+            x = S.activations(m, t.k, 600 + step)
+            y = w12.gemm(to_dev(x), t, ws=ws)
+            torch.cuda.synchronize()
+            bad, worst = O.gemm_check(x, w, y.cpu().numpy())
+            assert bad == 0, f"step {step} M={m}: {bad} outputs outside tolerance (worst rel {worst:.3g})"
+        assert int(ws[:cb].count_nonzero()) == 0, f"step {step}: arrival counters must return to zero"
+    assert sorted(set(plans)) == [1, 2, 3], plans   # GEMV, MFMA tiles and wide tiles all ran
