@@ -170,6 +170,21 @@ int w12_gemm_q(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
                float *Y, int64_t ldy, void *ws, uint64_t ws_bytes, hipStream_t stream);
 
 /*
+ * w12_gemm for callers that cannot allocate device memory: code under stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
+ * layouts, errors, tolerance and result as w12_gemm: Y is bitwise identical to w12_gemm's for
+ * the same operands.  The workspace is a 32 MiB array held by the library on each device (kept
+ * until the process ends); it covers every M <= 64 (the streaming tiles) at the default launch
+ * shape, and a product whose plan needs more is rejected with W12_ERR_WORKSPACE_TOO_SMALL (call w12_gemm
+ * with a workspace instead).  Nothing is allocated: the first call on a device looks up the
+ * array's address and clears its counter region on `stream` (a kernel launch); every call
+ * leaves it clear.  All calls on one device share the one array, so calls that overlap in time
+ * on one device (on different streams or host threads) race.
+ */
+int w12_gemm_noalloc(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
+                     float *Y, int64_t ldy, hipStream_t stream);
+
+/*
  * Grouped launch: several independent products of the same M in one launch (summary page
  * method bullet of section 4.1: the W12 GEMM is a stream-K GEMM whose split is reduced in a
  * fixed order).  items[i] asks for Y_i = X_i . W_i^T exactly as w12_gemm would (same operand

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     file_index,
     GROUP_MAX,
     gemm,
+    gemm_noalloc,
     gemm_group,
     gemm_group_workspace,
     gemm_group_workspace_size,

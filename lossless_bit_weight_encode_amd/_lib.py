@@ -59,6 +59,7 @@ _SIGNATURES = {
     "w12_gemm_workspace_init": (ctypes.c_int, [_c_p, _c_u64, _c_p]),
     "w12_gemm": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
     "w12_gemm_q": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p, _c_u64, _c_p]),
+    "w12_gemm_noalloc": (ctypes.c_int, [_c_p, _c_i32, _c_i64, ctypes.POINTER(_Tensor), _c_p, _c_i64, _c_p]),
     "w12_gemm_plan": (ctypes.c_int, [_c_i32, _c_i32, _c_i32, ctypes.POINTER(_PlanInfo)]),
     "w12_gemm_group_workspace_size": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), ctypes.POINTER(_c_u64)]),
     "w12_gemm_group": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_GemmItem), _c_p, _c_u64, _c_p]),
@@ -295,6 +296,17 @@ def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch
     name = "w12_gemm_q" if qpass else "w12_gemm"
     _check(name, getattr(lib(), name)(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
                                       _stream(stream)))
+    return y
+
+
+def gemm_noalloc(x: torch.Tensor, t: W12Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """w12_gemm_noalloc: the product of gemm() into a caller-provided Y, with the library's own
+    per-device workspace (no device allocation)."""
+    _require_cuda(x, y)
+    _bits16(x)
+    d = t.descriptor()
+    _check("w12_gemm_noalloc", lib().w12_gemm_noalloc(_ptr(x), x.shape[0], _pitch(x), ctypes.byref(d), _ptr(y),
+                                                       _pitch(y), _stream(stream)))
     return y
 
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libw12.so")
 ARCH = os.environ.get("W12_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["w12_encode.hip", "w12_decode.hip", "w12_gemm.hip", "w12_gemm_wide.hip", "w12_probe.hip", "w12_api.cpp", "w12_file.cpp"]
+SOURCES = ["w12_encode.hip", "w12_decode.hip", "w12_gemm.hip", "w12_gemm_wide.hip", "w12_probe.hip", "w12_noalloc.hip", "w12_api.cpp", "w12_file.cpp"]
 
 COMMON = [
     f"--offload-arch={ARCH}",

@@ -200,6 +200,23 @@ int w12_gemm_q(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, f
   return gemm_call(X, M, ldx, t, Y, ldy, ws, ws_bytes, true, stream);
 }
 
+int w12_gemm_noalloc(const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y, int64_t ldy,
+                     hipStream_t stream) {
+  int rc = check_tensor(t);
+  if (rc) return rc;
+  if (M < 1 || M > kMaxM) return fail(W12_ERR_UNSUPPORTED_SHAPE, "M=%d outside 1..%d", M, kMaxM);
+  const w12::GemmPlan p = w12::plan_gemm(M, t->N, t->K);
+  if (p.ws_bytes > w12::kScratchBytes)
+    return fail(W12_ERR_WORKSPACE_TOO_SMALL,
+                "M=%d, N=%d, K=%d needs %llu bytes of workspace, above the library's %llu-byte scratch; "
+                "call w12_gemm with a workspace", M, t->N, t->K, (unsigned long long)p.ws_bytes,
+                (unsigned long long)w12::kScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = w12::scratch_workspace(&ws, stream);
+  if (e != hipSuccess) return hip_status(e, "gemm_noalloc scratch");
+  return gemm_call(X, M, ldx, t, Y, ldy, ws, w12::kScratchBytes, false, stream);
+}
+
 // Validates a group and plans it; on success fills tiles_of / upt_of and *plan.
 static int group_plan(int32_t M, int32_t count, const w12_gemm_item* items, w12::GemmPlan* plan, int64_t* tiles_of,
                       int64_t* upt_of) {

@@ -63,6 +63,11 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream);
 
+// The GEMM workspace held in the library (w12_noalloc.hip): kScratchBytes per device, its
+// counter region cleared on the stream of the first call on that device.
+constexpr uint64_t kScratchBytes = uint64_t(32) << 20;
+hipError_t scratch_workspace(void** ws, hipStream_t stream);
+
 // Measurement aid: a plain streaming read of `bytes` bytes (w12_probe.hip).
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, int32_t loads_per_lane, int64_t grid, uint32_t* sink,
                              hipStream_t stream);
