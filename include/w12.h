@@ -1,14 +1,15 @@
 /*
  * w12.h - C ABI of libw12: the W12 lossless 12-bit BF16 weight format on MI355X (gfx950).
  *
- * W12 (SpecPilot, arXiv 2611.02501; summary page, method bullet of section 4.1, and the
- * news article part "(1) W12") stores each BF16 weight of an output channel as
- *   sign (1 bit) | exponent offset inside a 16-binade window chosen per channel (4 bits) |
- *   mantissa (7 bits),
- * and keeps weights outside the window, zeros, denormals and inf/NaN in an exact escape
- * list.  Every decoded tensor is checked bit for bit at load time (summary page, result
- * bullet of section 4.1), and the GEMM decodes the records in registers and reduces its
- * split in a fixed order, so it is deterministic (method bullet of section 4.1).
+ * The format (SpecPilot, arXiv 2611.02501; summary page, method bullet of section 4.1, and
+ * the news article part "(1) W12"): a 12-bit record per BF16 weight,
+ *   sign (1 bit) | exponent minus the channel's window base (4 bits, a window of 16
+ *   binades per output channel) | top 7 mantissa bits,
+ * plus an exact side list (the escapes) for weights the record cannot hold: exponents
+ * outside the window, zeros, subnormals and inf/NaN.  Loading compares each decoded tensor
+ * with its source bit for bit (summary page, result bullet of section 4.1); the GEMM decodes
+ * records in registers and reduces its K split in a fixed order, so its bits repeat from run
+ * to run (method bullet of section 4.1).
  *
  * Logical format (what every result is defined on):
  *   base[n]        window base exponent field b_n in 1..239; the window is [b_n, b_n+15].
@@ -67,7 +68,7 @@ typedef struct w12_tensor {
   int32_t N, K;          /* logical shape of W[N][K]                                     */
   int32_t layout;        /* W12_LAYOUT_RB16_K16                                          */
   int32_t reserved;      /* must be 0                                                    */
-  int64_t num_escapes;   /* E = esc_ptr[N]                                               */
+  int64_t num_escapes;   /* E = esc_ptr[N], below 2^30                                   */
   uint8_t *base;         /* [N]                                                          */
   uint8_t *hi;           /* [w12_layout_bytes().hi_bytes]                                */
   uint8_t *lo;           /* [w12_layout_bytes().lo_bytes]                                */

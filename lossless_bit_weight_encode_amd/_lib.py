@@ -204,16 +204,20 @@ def encode_emit(w: torch.Tensor, t: W12Tensor, stream=None) -> None:
 
 
 def encode(w: torch.Tensor, forced_base: torch.Tensor | None = None, stream=None) -> W12Tensor:
-    """BF16 [N, K] on the GPU -> W12Tensor.  Reads E back once (one synchronisation)."""
+    """BF16 [N, K] on the GPU -> W12Tensor.  Reads E back once (one synchronisation).
+
+    With a stream, everything (allocations, kernels, the read-back of E) runs on that stream;
+    w and forced_base must be ready on it."""
     _require_cuda(w)
     _bits16(w)
-    n, k = w.shape
-    base, hi, lo, esc_ptr = alloc_planes(n, k, w.device)
-    encode_count(w, base, esc_ptr, forced_base, stream)
-    e = int(esc_ptr[n].item()) & 0xFFFFFFFF
-    esc = torch.empty(e, dtype=torch.int32, device=w.device)
-    t = W12Tensor(n, k, base, hi, lo, esc_ptr, esc)
-    encode_emit(w, t, stream)
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        n, k = w.shape
+        base, hi, lo, esc_ptr = alloc_planes(n, k, w.device)
+        encode_count(w, base, esc_ptr, forced_base)
+        e = int(esc_ptr[n].item()) & 0xFFFFFFFF   # copies and waits on the same stream
+        esc = torch.empty(e, dtype=torch.int32, device=w.device)
+        t = W12Tensor(n, k, base, hi, lo, esc_ptr, esc)
+        encode_emit(w, t)
     return t
 
 
@@ -235,10 +239,12 @@ def verify_async(t: W12Tensor, ref: torch.Tensor, result: torch.Tensor, stream=N
 
 
 def verify(t: W12Tensor, ref: torch.Tensor, stream=None) -> tuple[int, int]:
-    """(mismatch count, first bad flat index or -1); synchronises to read the result."""
-    result = torch.empty(2, dtype=torch.int64, device=ref.device)
-    verify_async(t, ref, result, stream)
-    cnt, first = (int(v) for v in result.cpu().tolist())
+    """(mismatch count, first bad flat index or -1); synchronises to read the result.  With a
+    stream, the result buffer, the check and the read-back all run on that stream."""
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        result = torch.empty(2, dtype=torch.int64, device=ref.device)
+        verify_async(t, ref, result)
+        cnt, first = (int(v) for v in result.cpu().tolist())
     return cnt, (-1 if first == -1 else first)
 
 
@@ -283,19 +289,21 @@ def gemm(x: torch.Tensor, t: W12Tensor, y: torch.Tensor | None = None, ws: torch
     8-bit view, w12_gemm_q).
 
     ws: a workspace from gemm_workspace() (or any buffer of at least gemm_workspace_size bytes
-    initialised once with gemm_workspace_init); one is allocated here when omitted."""
+    initialised once with gemm_workspace_init); one is allocated here when omitted.  With a
+    stream, Y and the workspace allocated here belong to that stream."""
     _require_cuda(x)
     _bits16(x)
     m = x.shape[0]
-    if y is None:
-        y = torch.empty(m, t.n, dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = gemm_workspace(m, t.n, t.k, x.device, stream)
-    wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    d = t.descriptor()
-    name = "w12_gemm_q" if qpass else "w12_gemm"
-    _check(name, getattr(lib(), name)(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
-                                      _stream(stream)))
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        if y is None:
+            y = torch.empty(m, t.n, dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = gemm_workspace(m, t.n, t.k, x.device)
+        wsb = 0 if ws is None else ws.numel() * ws.element_size()
+        d = t.descriptor()
+        name = "w12_gemm_q" if qpass else "w12_gemm"
+        _check(name, getattr(lib(), name)(_ptr(x), m, _pitch(x), ctypes.byref(d), _ptr(y), _pitch(y), _ptr(ws), wsb,
+                                          _stream()))
     return y
 
 
@@ -367,14 +375,15 @@ def gemm_group(xs, ts, ys=None, ws: torch.Tensor | None = None, stream=None, qpa
     m = xs[0].shape[0] if xs else 0
     if any(x.shape[0] != m for x in xs):
         raise ValueError("every X of a group has the same number of rows")
-    if ys is None:
-        ys = [torch.empty(m, t.n, dtype=torch.float32, device=xs[0].device) for t in ts]
-    _require_cuda(*ys)
-    if ws is None:
-        ws = gemm_group_workspace(m, ts, xs[0].device, stream)
-    items, _descs = _group_items(xs, ts, ys)
-    name = "w12_gemm_group_q" if qpass else "w12_gemm_group"
-    _check(name, getattr(lib(), name)(m, len(ts), items, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        if ys is None:
+            ys = [torch.empty(m, t.n, dtype=torch.float32, device=xs[0].device) for t in ts]
+        _require_cuda(*ys)
+        if ws is None:
+            ws = gemm_group_workspace(m, ts, xs[0].device)
+        items, _descs = _group_items(xs, ts, ys)
+        name = "w12_gemm_group_q" if qpass else "w12_gemm_group"
+        _check(name, getattr(lib(), name)(m, len(ts), items, _ptr(ws), ws.numel() * ws.element_size(), _stream()))
     return ys
 
 

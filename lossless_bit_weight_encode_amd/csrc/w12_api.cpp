@@ -61,6 +61,9 @@ int check_tensor(const w12_tensor* t) {
   if (!t->base || !t->hi || !t->lo || !t->esc_ptr) return fail(W12_ERR_INVALID_ARG, "tensor has a NULL plane");
   if (t->num_escapes < 0 || t->num_escapes > (int64_t)t->N * t->K)
     return fail(W12_ERR_INVALID_ARG, "num_escapes=%lld outside 0..N*K", (long long)t->num_escapes);
+  // the kernels address the escape list with 32-bit byte offsets
+  if (t->num_escapes >= (int64_t(1) << 30))
+    return fail(W12_ERR_UNSUPPORTED_SHAPE, "num_escapes=%lld must be below 2^30", (long long)t->num_escapes);
   if (t->num_escapes > 0 && !t->esc) return fail(W12_ERR_INVALID_ARG, "esc is NULL with num_escapes > 0");
   if (!aligned(t->hi, 16) || !aligned(t->lo, 16)) return fail(W12_ERR_MISALIGNED, "hi and lo must be 16-byte aligned");
   if (!aligned(t->esc_ptr, 4) || (t->esc && !aligned(t->esc, 4))) return fail(W12_ERR_MISALIGNED, "esc_ptr/esc must be 4-byte aligned");

@@ -1,8 +1,8 @@
 // W12 GEMM: Y[M][N] = X[M][K] . W[N][K]^T with BF16 X, W12 weights and FP32 accumulation.
 //
-// SpecPilot summary page, method bullet of section 4.1: the W12 GEMM is a stream-K GEMM that
-// decodes the records in registers and splits the reduction in a fixed order, so it is
-// deterministic.  This gfx950 version:
+// What the GEMM must do is set by the SpecPilot summary page, method bullet of section 4.1:
+// decode W12 records in registers inside a stream-K GEMM, and reduce the K split in an order
+// fixed in advance, so repeated runs give identical bits.  This gfx950 version:
 //   * streams the hi/lo record planes from HBM into a per-wave two-stage LDS ring with
 //     buffer-to-LDS DMA loads (no registers held while a stage is in flight), reads each
 //     lane's 16 + 8 bytes back, decodes them to BF16 pairs in registers (decode16) and

@@ -2,8 +2,9 @@
 // verification: 128 rows and more), where the product is bound by the matrix cores rather
 // than by the weight stream.
 //
-// SpecPilot summary page, method bullet of section 4.1: the W12 GEMM decodes the records in
-// registers and splits the reduction in a fixed order, so it is deterministic.  The streaming
+// Requirements from the SpecPilot summary page, method bullet of section 4.1: decode in
+// registers, and a K split reduced in an order fixed in advance (identical bits run to run).
+// The streaming
 // kernel re-reads W once per 64 rows of X; this one reads it once per 128 or 256 rows:
 //   * a work-group of 8 waves owns a tile of 64 TM rows of X (TM = 2 or 4) x 256 channels;
 //     wave (wm, wn) owns rows 32 TM wm .. +32 TM and channels 64 wn .. +64, as TM x 2

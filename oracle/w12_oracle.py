@@ -8,21 +8,23 @@ definition so that a reader can check it against the pages by eye.
 
 Sources (SpecPilot, arXiv 2611.02501, as summarised on its web pages):
 
-* [S4.1-method]  summary page, method bullet attributed to section 4.1: W12 stores
-  each weight as a sign bit, a 4-bit exponent offset within a 16-binade window per
-  output channel, and seven mantissa bits, with an exact escape list for
-  out-of-window weights, zeros and denormals; its GEMM decodes records in
-  registers and splits the reduction in a fixed order so it is deterministic.
-* [S4.1-result]  summary page, result bullet attributed to section 4.1: about
-  12.01-12.02 bits per weight on eight dense models; every decoded tensor is
-  checked bit for bit at load time.
-* [Article-W12]  news article, part "(1) W12": BF16 exponents cluster within an
-  output channel; each weight becomes 12 bits (sign, 4-bit exponent offset, 7-bit
-  mantissa); weights whose exponent lies outside the preset range go to a sparse
-  list and are restored exactly; the original weights are recovered bit for bit.
-* [Article-TLV]  news article, part "(3) two-level verification": the first pass
-  verifies at low precision with the 8-bit weight view nested in W12, yields a
-  candidate chain but accepts nothing; only the later exact pass accepts tokens.
+* [S4.1-method]  summary page, method bullet of section 4.1.  Fixes the record: one
+  sign bit, the exponent as a four-bit offset from a base chosen per output channel
+  (so one channel's window spans sixteen binades), and the top seven mantissa bits.
+  Exponents outside the window, zeros and subnormals are not representable there
+  and go to an exact side list.  The GEMM decodes in registers and reduces its K
+  split in a fixed order, which makes its result reproducible.
+* [S4.1-result]  summary page, result bullet of section 4.1.  Gives the storage cost
+  (a little over twelve bits per weight, averaged over eight dense models) and
+  states that each decoded tensor is compared with its source bit for bit when it
+  is loaded.
+* [Article-W12]  news article, part "(1) W12".  Motivates the window (within one
+  output channel the BF16 exponents sit close together), gives the same twelve-bit
+  split, and says the side list restores the remaining weights exactly, so the
+  source tensor comes back unchanged.
+* [Article-TLV]  news article, part "(3) two-level verification".  The first of two
+  verification passes runs on the eight-bit view contained in each W12 record and
+  only proposes a chain of candidate tokens; tokens are accepted by the exact pass.
 
 Readings where the pages are silent (each is also listed in the design notes):
 

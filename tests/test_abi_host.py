@@ -69,6 +69,16 @@ def call_gemm(x=0x10000, m=4, ldx=64, d=None, y=0x20000, ldy=64, ws=None, ws_byt
     return w12.lib().w12_gemm(x, m, ldx, ctypes.byref(d), y, ldy, ws, ws_bytes, None)
 
 
+def test_escape_count_limit():
+    """E >= 2^30 is rejected before any launch (the kernels use 32-bit byte offsets into the
+    escape list); E = 2^30 - 1 passes the tensor check and fails later on a NULL workspace."""
+    big = dict(n=1 << 16, k=1 << 15)
+    assert call_gemm(d=_desc(e=1 << 30, **big), ldx=1 << 15, ldy=1 << 16) == -2
+    assert "2^30" in w12.lib().w12_last_error().decode()
+    assert call_gemm(d=_desc(e=(1 << 30) - 1, **big), ldx=1 << 15, ldy=1 << 16, m=16) in (-1, -3)
+    assert w12.lib().w12_decode(ctypes.byref(_desc(e=1 << 30, **big)), 0x10000, 1 << 15, None) == -2
+
+
 def test_gemm_argument_validation():
     lib = w12.lib()
     assert call_gemm(x=None) == -1

@@ -416,3 +416,32 @@ def test_gemm_large_m(m):
     y = w12.gemm(to_dev(x), t).cpu().numpy()
     bad, worst = O.gemm_check(x, w, y)
     assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
+
+
+def test_side_stream_encode_verify_gemm():
+    """Every binding call on a non-default stream: encode (its read-back of the escape count),
+    verify (its read-back of the result) and the GEMM with its own workspace all run on that
+    stream and give the same results as on the default stream.  A long kernel queued on the
+    default stream first would expose a read-back taken on the wrong stream."""
+    w, _ = case("gauss_300x4096")
+    n, k = w.shape
+    wd = dev_weights(w)
+    x = to_dev(S.activations(16, k, 4242))
+    t_ref = w12.encode(wd)
+    y_ref = w12.gemm(x, t_ref)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    # keep the default stream busy, so work that wrongly lands there would be visibly late
+    busy = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    for _ in range(20):
+        busy.mul_(1.0001)
+    t = w12.encode(wd, stream=s)
+    assert t.num_escapes == t_ref.num_escapes
+    assert w12.verify(t, wd, stream=s) == (0, -1)
+    y = w12.gemm(x, t, stream=s)
+    s.synchronize()
+    assert torch.equal(y, y_ref)
+    for name in ("base", "hi", "lo", "esc_ptr", "esc"):
+        assert torch.equal(getattr(t, name), getattr(t_ref, name)), name
+    torch.cuda.synchronize()
