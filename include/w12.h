@@ -175,8 +175,8 @@ int w12_gemm_q(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor *t,
  * serving loops, harnesses that forbid hipMalloc.  Same arguments (minus the workspace),
  * layouts, errors, tolerance and result as w12_gemm: Y is bitwise identical to w12_gemm's for
  * the same operands.  The workspace is a 32 MiB array held by the library on each device (kept
- * until the process ends); it covers every M <= 64 (the streaming tiles) at the default launch
- * shape, and a product whose plan needs more is rejected with W12_ERR_WORKSPACE_TOO_SMALL (call w12_gemm
+ * until the process ends); it covers every M <= 64 (the streaming tiles) with K <= 64,000 at the
+ * default launch shape, and a product whose plan needs more is rejected with W12_ERR_WORKSPACE_TOO_SMALL (call w12_gemm
  * with a workspace instead).  Nothing is allocated: the first call on a device looks up the
  * array's address and clears its counter region on `stream` (a kernel launch); every call
  * leaves it clear.  All calls on one device share the one array, so calls that overlap in time
@@ -285,8 +285,14 @@ int w12_file_load(const char *path, int32_t count, const int32_t *which, const w
 int w12_read_probe(const void *buf, uint64_t bytes, int32_t loads_per_lane, int32_t groups_per_cu,
                    uint32_t *sink, hipStream_t stream);
 
-/* Stored bits per weight: (1.5*N*K + N + 4*(N+1) + 4*E) * 8 / (N*K). */
+/* Stored bits per weight: (1.5*N*K + N + 4*(N+1) + 4*E) * 8 / (N*K).  -1 for N < 1, K < 1
+ * or E < 0. */
 double w12_bits_per_weight(int32_t N, int32_t K, int64_t E);
+
+/* Bytes of the logical format for W[N][K] with E escapes: ceil(12 N K / 8) record bytes, one
+ * base byte per channel, (N + 1) 4-byte escape pointers and 4 bytes per escape.  0 for N < 1,
+ * K < 1 or E < 0.  (The device planes are padded to whole 16 x 16 chunks: w12_layout_bytes.) */
+uint64_t w12_tensor_bytes(int32_t N, int32_t K, int64_t E);
 
 const char *w12_status_string(int status);
 const char *w12_last_error(void);

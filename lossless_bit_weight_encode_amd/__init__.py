@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     gemm_workspace_init,
     gemm_workspace_size,
     layout_bytes,
+    tensor_bytes,
     lib,
     load,
     read_probe,

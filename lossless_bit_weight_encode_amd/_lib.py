@@ -70,6 +70,7 @@ _SIGNATURES = {
                                      _c_u64, ctypes.POINTER(_c_p), ctypes.POINTER(_c_i64), _c_p, _c_p]),
     "w12_read_probe": (ctypes.c_int, [_c_p, _c_u64, _c_i32, _c_i32, _c_p, _c_p]),
     "w12_bits_per_weight": (ctypes.c_double, [_c_i32, _c_i32, _c_i64]),
+    "w12_tensor_bytes": (_c_u64, [_c_i32, _c_i32, _c_i64]),
     "w12_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "w12_last_error": (ctypes.c_char_p, []),
 }
@@ -174,8 +175,8 @@ class W12Tensor:
         return bits_per_weight(self.n, self.k, self.num_escapes)
 
     def nbytes(self) -> int:
-        """Bytes of the logical format: 1.5 per weight + base + pointers + 4 per escape."""
-        return int(1.5 * self.n * self.k) + self.n + 4 * (self.n + 1) + 4 * self.num_escapes
+        """Bytes of the logical format (w12_tensor_bytes)."""
+        return tensor_bytes(self.n, self.k, self.num_escapes)
 
 
 def alloc_planes(n: int, k: int, device) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
@@ -331,6 +332,10 @@ def read_probe(buf: torch.Tensor, nbytes: int, loads_per_lane: int, groups_per_c
 
 def bits_per_weight(n: int, k: int, e: int) -> float:
     return float(lib().w12_bits_per_weight(n, k, e))
+
+
+def tensor_bytes(n: int, k: int, e: int) -> int:
+    return int(lib().w12_tensor_bytes(n, k, e))
 
 
 def _group_items(xs, ts, ys):

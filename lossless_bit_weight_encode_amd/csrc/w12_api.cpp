@@ -365,6 +365,12 @@ double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {
   return (1.5 * nk + (double)N + 4.0 * ((double)N + 1.0) + 4.0 * (double)E) * 8.0 / nk;
 }
 
+uint64_t w12_tensor_bytes(int32_t N, int32_t K, int64_t E) {
+  if (N < 1 || K < 1 || E < 0) return 0;
+  const uint64_t nk = (uint64_t)N * (uint64_t)K;
+  return (12 * nk + 7) / 8 + (uint64_t)N + 4 * ((uint64_t)N + 1) + 4 * (uint64_t)E;
+}
+
 const char* w12_status_string(int status) {
   switch (status) {
     case W12_OK: return "ok";

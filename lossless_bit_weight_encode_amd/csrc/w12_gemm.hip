@@ -1108,6 +1108,20 @@ static int groups_per_cu(int path, int M, int m_tile) {
 // for every M <= 16.  W12_GEMV_MAX_M (0..8) moves the boundary, e.g. 8 for the wavefront
 // reduction at every M <= 8.
 constexpr int kGemvMaxM = 2;
+
+// Longest stretch of one tile (in units of 256 k) that a work-group may sum on its own: each
+// lane then chains at most 16 products per unit, 4000 in all, which with the few cross-lane,
+// cross-wave and split-K levels keeps every output's serial summation depth below 4096.
+constexpr int64_t kMaxChainUnits = 250;
+
+// Raise the grid so that no work-group range holds more than kMaxChainUnits units (only K
+// above 64,000 needs it).
+static int64_t chain_bound_grid(int64_t G, int64_t units, int64_t upt) {
+  if (upt <= kMaxChainUnits) return G;
+  int64_t need = ceil_div(units, kMaxChainUnits);
+  need = need < kMaxGrid ? need : kMaxGrid;
+  return G > need ? G : need;
+}
 // Smallest M that runs the wide tiles (W read once per 128 or 256 rows of X instead of once
 // per 64).  W12_WIDE_MIN_M moves it.
 constexpr int kWideMinM = 65;
@@ -1152,6 +1166,7 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
     const int64_t s = G / p.tiles;
     if (4 * p.tiles * s >= 3 * G) G = p.tiles * s;
   }
+  G = chain_bound_grid(G, p.units, p.upt);
   p.grid = G;
   // most segments (work-group ranges) meeting one tile: 1 + the range starts strictly inside it
   {
@@ -1317,6 +1332,7 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
   if (G > kMaxGrid) G = kMaxGrid;
   if (G > p.units) G = p.units;
   if (G < 1) G = 1;
+  for (int i = 0; i < count; ++i) G = chain_bound_grid(G, p.units, upt_of[i]);
   p.grid = G;
   // most segments meeting one tile
   {

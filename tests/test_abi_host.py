@@ -41,6 +41,27 @@ def test_bits_per_weight_matches_definition(n, k, e):
     assert w12.bits_per_weight(n, k, e) == pytest.approx(O.bits_per_weight(n, k, e), rel=1e-15)
 
 
+@pytest.mark.parametrize("n,k,e", [(1, 16, 0), (34816, 5120, 29837), (3, 5, 7), (5120, 17408, 1800594)])
+def test_tensor_bytes_matches_definition(n, k, e):
+    """w12_tensor_bytes = the oracle's bits per weight x N K / 8 (rounded up to whole bytes)."""
+    import math
+    assert w12.tensor_bytes(n, k, e) == math.ceil(O.bits_per_weight(n, k, e) * n * k / 8 - 1e-6)
+    assert w12.tensor_bytes(0, k, e) == 0 and w12.tensor_bytes(n, k, -1) == 0
+
+
+@pytest.mark.parametrize("m,n", [(1, 64), (1, 65520), (16, 65520), (33, 4096), (100, 65520), (256, 65520)])
+def test_long_k_is_always_split(m, n):
+    """At K = 65,536 (256 units of 256 k per tile) no work-group range holds more than 250
+    units, so a lane chains at most 4,000 products and the summation depth stays below 4,096."""
+    k = 65536
+    p = w12.gemm_plan(m, n, k)
+    rb = 16 if p["path"] == 3 else 4
+    tiles = ((n + 15) // 16 + rb - 1) // rb * ((m + p["m_tile"] - 1) // p["m_tile"])
+    units = tiles * 256
+    assert -(-units // p["grid"]) <= 250
+    assert p["splits"] >= 2
+
+
 def test_layout_bytes():
     assert w12.layout_bytes(256, 512) == (256 * 512, 256 * 512 // 2)
     # ragged N and K are padded to 16 rows x 16 k
