@@ -69,7 +69,10 @@ def test_bits_per_weight_hand(case):
 
 
 def _as_float(v):
-    return float(v) if not isinstance(v, str) else float(v)
+    """A JSON number, or a string: "inf", "-inf", "nan", or an exact hexadecimal float."""
+    if not isinstance(v, str):
+        return float(v)
+    return float.fromhex(v) if "0x" in v else float(v)
 
 
 @pytest.mark.parametrize("case", _load("w12_hand_gemm.json")["cases"], ids=lambda c: c["name"])
@@ -84,7 +87,7 @@ def test_gemm_hand(case):
     assert np.array_equal(np.isnan(y), np.isnan(exp))
     assert np.array_equal(y[np.isinf(exp)], exp[np.isinf(exp)])
     if "a" in case:
-        assert np.array_equal(a, np.array(case["a"], dtype=np.float64))
+        assert np.array_equal(a, np.array([[_as_float(v) for v in row] for row in case["a"]], dtype=np.float64))
 
 
 # ---------------------------------------------------------------------------------------
