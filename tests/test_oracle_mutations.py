@@ -21,6 +21,13 @@ def _load(name):
         return json.load(f)
 
 
+def _num(v):
+    """A JSON number, or a string: "inf", "-inf", "nan", or an exact hexadecimal float."""
+    if not isinstance(v, str):
+        return float(v)
+    return float.fromhex(v) if "0x" in v else float(v)
+
+
 def pins_hold() -> bool:
     """Run a compact set of pins; False if any fails."""
     try:
@@ -41,13 +48,13 @@ def pins_hold() -> bool:
             x = np.array(case["x"], dtype=np.uint16)
             ww = np.array(case["w"], dtype=np.uint16)
             y, a = O.gemm_reference(x, ww)
-            exp = np.array([[float(v) for v in row] for row in case["y"]])
+            exp = np.array([[_num(v) for v in row] for row in case["y"]])
             assert y.shape == exp.shape
             fin = np.isfinite(exp)
             assert np.array_equal(y[fin], exp[fin])
             assert np.array_equal(np.isnan(y), np.isnan(exp))
             if "a" in case:
-                assert np.array_equal(a, np.array(case["a"], dtype=np.float64))
+                assert np.array_equal(a, np.array([[_num(v) for v in row] for row in case["a"]], dtype=np.float64))
         return True
     except (AssertionError, ValueError, IndexError):
         return False
@@ -118,9 +125,30 @@ def _mut_escape_order(mp):
     mp.setattr(O, "encode", enc)
 
 
+def _mut_subnormals_flushed(mp):
+    orig = O.bf16_to_f64
+
+    def conv(w):
+        v = orig(w)
+        return np.where((np.asarray(w, np.uint16) & 0x7F80) == 0, 0.0 * v, v)
+    mp.setattr(O, "bf16_to_f64", conv)
+
+
+def _mut_subnormal_implicit_bit(mp):
+    orig = O.bf16_to_f64
+
+    def conv(w):
+        w = np.asarray(w, np.uint16)
+        sub = ((w & 0x7F80) == 0) & ((w & 0x7F) != 0)
+        sign = np.where(w & 0x8000, -1.0, 1.0)
+        return np.where(sub, sign * (1.0 + (w & 0x7F) / 128.0) * 2.0 ** -126, orig(w))
+    mp.setattr(O, "bf16_to_f64", conv)
+
+
 @pytest.mark.parametrize("mutation", [
     _mut_window15, _mut_bmax, _mut_tie_largest, _mut_offset_off_by_one, _mut_sign_dropped,
     _mut_gemm_transposed, _mut_gemm_abs_dropped, _mut_bpw_no_pointer, _mut_escape_order,
+    _mut_subnormals_flushed, _mut_subnormal_implicit_bit,
 ], ids=lambda f: f.__name__)
 def test_planted_mistake_is_caught(monkeypatch, mutation):
     mutation(monkeypatch)
