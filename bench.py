@@ -144,6 +144,13 @@ def main():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-legs", action="store_true",
+                    help="only the oracle on the host cores, for the tiny case, the tree-verify M sweep, the batched "
+                         "M and heavy-tail matrices, and the full model streamed one layer at a time (no GPU; "
+                         "several minutes); prints one JSON line")
+    ap.add_argument("--cpu-layers", nargs=2, type=int, metavar=("FIRST", "END"),
+                    help="with --cpu-legs: only the full-model leg, over layers FIRST..END-1 (so the whole model can "
+                         "be timed in parts whose totals add up)")
     ap.add_argument("--no-full-model", action="store_true", help="skip the 64-layer weight stream")
     ap.add_argument("--model-layers", type=int, default=S.FULL_MODEL_LAYERS)
     ap.add_argument("--only-layer", action="store_true", help="time only the layer steps (for profiling)")
@@ -189,12 +196,22 @@ def main():
                     help="sweep the plain streaming-read kernel (loads in flight x work-groups per CU) and exit")
     ap.add_argument("--probe-reps", type=int, default=3,
                     help="launches per case of --valu-probe (the counter summaries expect 3)")
+    ap.add_argument("--r13-probe", action="store_true",
+                    help="gate_up and down at M = 1..8, once through the wavefront GEMV (W12_GEMV_MAX_M=8) and once "
+                         "through the 16-row MFMA tiles (W12_GEMV_MAX_M=0), --probe-reps launches each; prints the "
+                         "event times as JSON")
+    ap.add_argument("--summarize-r13-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace run of --r13-probe into the GEMV-vs-MFMA summary under "
+                         "profiles/")
     ap.add_argument("--summarize-sweep-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
                     help="turn a rocprofv3 --kernel-trace run of --valu-probe into the per-M kernel-time summary "
                          "under profiles/")
     args = ap.parse_args()
     if args.summarize_sweep_trace:
         summarize_sweep_trace(*args.summarize_sweep_trace)
+        return
+    if args.summarize_r13_trace:
+        summarize_r13_trace(*args.summarize_r13_trace)
         return
     if args.summarize_encode_lds:
         summarize_encode_lds(*args.summarize_encode_lds)
@@ -224,6 +241,10 @@ def main():
         print(f"bench.py measures one GPU only (the W12 path is built and timed on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_legs:
+        rng = tuple(args.cpu_layers) if args.cpu_layers else None
+        print(json.dumps(cpu_legs(args.model_layers, rng)))
+        return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.init()
     dev = torch.device("cuda:0")
@@ -234,6 +255,9 @@ def main():
         return
     if args.valu_probe:
         gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M, args.probe_reps)
+        return
+    if args.r13_probe:
+        gemm_probe(dev, stream, R13_MATS, R13_M, args.probe_reps, gemv_max=(8, 0))
         return
     if args.read_probe:
         variants = [(u, g) for u in (1, 2, 4, 8, 16) for g in (1, 2, 4, 8)]
@@ -337,6 +361,9 @@ def main():
     rec["on"] = True
     t_step_instr = timed(layer_step, args.steps, stream)
     rec["on"] = False
+    # Y of the last timed step, kept on the host for the oracle check after all timing
+    torch.cuda.synchronize()
+    y_timed = {nm: y_dev[nm].cpu().numpy() for nm in names}
     gate_us = [a.elapsed_time(b) * 1e3 for a, b in ev_pairs]
     weight_bytes = sum(2 * n * k for n, k in (S.LAYER_SHAPES[nm] for nm in names))
     moved = sum(alg_bytes(*S.LAYER_SHAPES[nm], m_step, enc[nm].num_escapes) for nm in names)
@@ -461,18 +488,29 @@ def main():
     out["hot_cache"] = {"what": "the same encoded copy launched 30 times in a row at M=16: matrices under the "
                                 "256 MB Infinity Cache are served from it", **hot}
 
+    # encoded copies of one matrix rotated by the sweep legs: at least 1 GiB, so no launch finds
+    # its weights in the 256 MB Infinity Cache
+    rot = {}
+    if not args.no_sweep:
+        for nm in ("gate_up", "down"):
+            cs = [c[nm] for c in copies]
+            while sum(t.nbytes() for t in cs) < (1 << 30):
+                cs.append(clone_tensor(enc[nm]))
+            rot[nm] = cs
+
     # ---- tree-verify M sweep on gate_up and down ----
     if not args.no_sweep:
-        sweep = {}
+        sweep = {"rotated_MB": {nm: round(sum(t.nbytes() for t in cs) / 1e6, 1) for nm, cs in rot.items()}}
         for nm in ("gate_up", "down"):
             n, k = S.LAYER_SHAPES[nm]
+            cs = rot[nm]
             for m in S.TREE_M_SWEEP + (16,):
                 x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
                 y = torch.empty(m, n, dtype=torch.float32, device=dev)
                 wsm = w12.gemm_workspace(m, n, k)
                 for i in range(3):
-                    w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm)
-                t = timed(lambda i: w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm), 30, stream)
+                    w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm)
+                t = timed(lambda i: w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm), 30, stream)
                 ab = alg_bytes(n, k, m, enc[nm].num_escapes)
                 fl = byte_floor_us(n, k, m, enc[nm].num_escapes)
                 sweep[f"{nm}_M{m}"] = {
@@ -486,16 +524,17 @@ def main():
 
     # ---- batched verify on gate_up and down (MFMA-bound tiles) ----
     if not args.no_sweep:
-        batched = {}
+        batched = {"rotated_MB": {nm: round(sum(t.nbytes() for t in cs) / 1e6, 1) for nm, cs in rot.items()}}
         for nm in ("gate_up", "down"):
             n, k = S.LAYER_SHAPES[nm]
+            cs = rot[nm]
             for m in S.BATCHED_M:
                 x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
                 y = torch.empty(m, n, dtype=torch.float32, device=dev)
                 wsm = w12.gemm_workspace(m, n, k)
                 for i in range(3):
-                    w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm)
-                t = timed(lambda i: w12.gemm(x, copies[i % len(copies)][nm], y=y, ws=wsm), 10, stream)
+                    w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm)
+                t = timed(lambda i: w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm), 10, stream)
                 fl = byte_floor_us(n, k, m, enc[nm].num_escapes)
                 plan = w12.gemm_plan(m, n, k)
                 batched[f"{nm}_M{m}"] = {
@@ -507,9 +546,13 @@ def main():
                 log(f"[bench] batched {nm} M={m}: {t * 1e3:.1f} us, {2 * m * n * k / t / 1e9:.0f} TFLOP/s")
         out["batched_verify"] = batched
 
+    # ---- escape stress: heavy-tailed weights with 2% out-of-window values (gate_up, down) ----
+    if not args.no_sweep:
+        out["heavy_tail"] = heavy_tail_leg(dev, stream, out.get("tree_sweep", {}), out.get("batched_verify", {}))
+
     # ---- full-model weight stream: 64 layers resident, 256 GEMMs at M=32 from cold weights ----
     if not args.no_full_model:
-        del copies
+        del copies, rot
         torch.cuda.empty_cache()
         out["full_model"] = full_model_leg(dev, stream, args.model_layers, 32)
 
@@ -531,7 +574,7 @@ def main():
 
     # ---- CPU oracle on the host cores (a reported baseline, not the target) ----
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(layer, enc)
+        out["cpu_baseline"] = cpu_baseline(layer, enc, y_timed)
     print(json.dumps(out))
 
 
@@ -548,16 +591,21 @@ def mfma_probe(dev, stream):
     gemm_probe(dev, stream, MFMA_PROBE_MATS, MFMA_PROBE_M)
 
 
-def gemm_probe(dev, stream, mats, ms, reps=3):
+def gemm_probe(dev, stream, mats, ms, reps=3, gemv_max=(None,)):
     """Layer 0's matrices in ``mats`` at every M of ``ms``, ``reps`` launches each on three rotating
-    encoded copies, in a fixed order (matrix-major); prints the per-launch event times."""
+    encoded copies, in a fixed order (matrix-major, then W12_GEMV_MAX_M values, then M); prints
+    the per-launch event times.  A gemv_max of None keeps the default GEMV / MFMA boundary."""
     layer = S.layer(0, which=mats)
     res = {}
     for nm in mats:
         n, k = S.LAYER_SHAPES[nm]
         e0 = w12.encode(dev_bits(layer[nm]))
         cs = [e0, clone_tensor(e0), clone_tensor(e0)]
-        for m in ms:
+        for gv, m in [(gv, m) for gv in gemv_max for m in ms]:
+            if gv is None:
+                os.environ.pop("W12_GEMV_MAX_M", None)
+            else:
+                os.environ["W12_GEMV_MAX_M"] = str(gv)
             x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
             y = torch.empty(m, n, dtype=torch.float32, device=dev)
             ws = w12.gemm_workspace(m, n, k)
@@ -568,13 +616,64 @@ def gemm_probe(dev, stream, mats, ms, reps=3):
                 b.record(stream)
             torch.cuda.synchronize()
             plan = w12.gemm_plan(m, n, k)
-            res[f"{nm}_M{m}"] = {"kernel": kernel_name(plan, m), "launch_us": [round(a.elapsed_time(b) * 1e3, 2)
-                                                                              for a, b in evs],
-                                 "flops": 2 * m * n * k, "grid": plan["grid"], "m_tile": plan["m_tile"],
-                                 "escapes": e0.num_escapes}
+            key = f"{nm}_M{m}" if gv is None else f"{nm}_M{m}_gemvmax{gv}"
+            res[key] = {"kernel": kernel_name(plan, m), "launch_us": [round(a.elapsed_time(b) * 1e3, 2)
+                                                                     for a, b in evs],
+                        "flops": 2 * m * n * k, "grid": plan["grid"], "m_tile": plan["m_tile"],
+                        "escapes": e0.num_escapes}
+        os.environ.pop("W12_GEMV_MAX_M", None)
         del cs, e0
         torch.cuda.empty_cache()
     print(json.dumps(res))
+
+
+R13_MATS = ("gate_up", "down")
+R13_M = tuple(range(1, 9))
+
+
+def summarize_r13_trace(trace_csv, probe_json, command):
+    """rocprofv3 kernel durations of the --r13-probe launches: the wavefront GEMV (GemvPath<M>)
+    against the 16-row MFMA tile (MfmaPath<1>) at M = 1..8 on gate_up and down, first launch of
+    each case dropped."""
+    import csv
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    gemm = [r for r in trace if "k_gemm" in r["Kernel_Name"]]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    med = {}
+    i = 0
+    for nm in R13_MATS:
+        for gv in (8, 0):
+            for m in R13_M:
+                info = probe[f"{nm}_M{m}_gemvmax{gv}"]
+                reps = len(info["launch_us"])
+                rows = gemm[i:i + reps][1:]
+                i += reps
+                assert all(info["kernel"].split("<")[1][:4] in r["Kernel_Name"] for r in rows), "trace out of order"
+                d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
+                med[(nm, gv, m)] = (float(np.median(d)), float(d.mean()), len(d), info["escapes"])
+    assert i == len(gemm), f"{len(gemm) - i} GEMM launches in the trace are not in the probe"
+    lines = ["# Wavefront GEMV against 16-row MFMA tiles at M = 1..8 (gate_up 34816 x 5120, down 5120 x 17408), "
+             "MI355X", "", "Command (run from the repository root):", "", "```", command, "```", "",
+             "Kernel trace durations (median and mean over the launches of each case, the first dropped; three "
+             "rotating encoded copies). `GemvPath<M>` is the FP32 dot2 wavefront GEMV (W12_GEMV_MAX_M=8), "
+             "`MfmaPath<1>` the bf16 MFMA 16-row tile (W12_GEMV_MAX_M=0). Fraction = algorithmic bytes of the "
+             "launch / median / 8 TB/s.", "",
+             "| matrix | M | GEMV median us | GEMV frac | MFMA median us | MFMA frac | faster |",
+             "|---|---|---|---|---|---|---|"]
+    for nm in R13_MATS:
+        n, k = S.LAYER_SHAPES[nm]
+        for m in R13_M:
+            g, f = med[(nm, 8, m)], med[(nm, 0, m)]
+            ab = alg_bytes(n, k, m, g[3])
+            lines.append(f"| {nm} | {m} | {g[0]:.2f} | {ab / g[0] / 1e3 / HBM_PEAK_GBPS:.3f} | {f[0]:.2f} | "
+                         f"{ab / f[0] / 1e3 / HBM_PEAK_GBPS:.3f} | {'GEMV' if g[0] < f[0] else 'MFMA'} "
+                         f"({abs(g[0] - f[0]) / max(g[0], f[0]) * 100:.1f}%) |")
+    path = os.path.join(ROOT, "profiles", "gemm_gemv_vs_mfma_M1_M8_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_mfma(pmc_csv, probe_json):
@@ -1114,10 +1213,52 @@ def summarize_counters(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def cpu_baseline(layer, enc):
+HEAVY_M = (16, 256, 512)
+
+
+def heavy_tail_leg(dev, stream, sweep, batched):
+    """GEMM times on the heavy-tail matrices (Student-t weights, 2% values 12..19 binades above the
+    bulk; seeds 1000 / 1001 as in the parity tests) at M = 16, 256, 512, over >= 1 GiB of rotated
+    encoded copies, with the ratio to the Gaussian matrix of the same shape and M."""
+    res = {}
+    for nm, seed in (("gate_up", 1000), ("down", 1001)):
+        n, k = S.LAYER_SHAPES[nm]
+        w = dev_bits(S.heavy_tail_weights(seed, n, k))
+        t0 = w12.encode(w)
+        del w
+        cs = [t0]
+        while sum(t.nbytes() for t in cs) < (1 << 30):
+            cs.append(clone_tensor(t0))
+        e = t0.num_escapes
+        res[nm] = {"escapes": e, "escape_frac": round(e / (n * k), 5), "bits_per_weight": round(t0.bits_per_weight(), 4),
+                   "rotated_MB": round(sum(t.nbytes() for t in cs) / 1e6, 1)}
+        for m in HEAVY_M:
+            x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
+            y = torch.empty(m, n, dtype=torch.float32, device=dev)
+            wsm = w12.gemm_workspace(m, n, k)
+            for i in range(3):
+                w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm)
+            t = timed(lambda i: w12.gemm(x, cs[i % len(cs)], y=y, ws=wsm), 10 if m > 64 else 30, stream)
+            ab = alg_bytes(n, k, m, e)
+            g = sweep.get(f"{nm}_M{m}") or batched.get(f"{nm}_M{m}")
+            res[nm][f"M{m}"] = {
+                "us": round(t * 1e3, 2), "weight_GBps": round(2 * n * k / t / 1e6, 1),
+                "moved_GBps": round(ab / t / 1e6, 1), "frac": round(ab / t / 1e6 / HBM_PEAK_GBPS, 4),
+                "over_gaussian": None if not g else round(t * 1e3 / g["us"], 3),
+            }
+            log(f"[bench] heavy {nm} M={m}: {t * 1e3:.1f} us ({res[nm][f'M{m}']['over_gaussian']} x gaussian)")
+        del cs, t0
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(layer, enc, y_timed):
     """The oracle's decode + FP64 GEMM of gate_up at M=16 (the whole matrix), timed 3 times on all
     host cores, once on one thread; and the oracle's encode and decode-compare (decode, then a
-    bit-for-bit comparison with the BF16 source) of the same matrix, timed once each."""
+    bit-for-bit comparison with the BF16 source) of the same matrix, timed once each.
+
+    The same leg checks the GPU's Y of the last timed layer step (untimed): every gate_up output
+    against the reference just computed, and 256 sampled channels of each other matrix."""
     from oracle import w12_oracle as O
     w = layer["gate_up"]
     n, k = w.shape
@@ -1132,10 +1273,12 @@ def cpu_baseline(layer, enc):
     t_cmp = time.perf_counter() - t0
     assert same, "oracle round trip failed"
 
+    last = {}
+
     def run():
         t0 = time.perf_counter()
         wd = O.decode(ref)
-        O.gemm_reference(x, wd)
+        last["ya"] = O.gemm_reference(x, wd)
         return time.perf_counter() - t0
 
     times = []
@@ -1143,6 +1286,20 @@ def cpu_baseline(layer, enc):
         times.append(run())
         log(f"[bench] cpu baseline rep {times[-1]:.2f}s")
     t = float(np.median(times))
+    # the timed GPU outputs against the oracle (after all timing)
+    y_ref, a_ref = last.pop("ya")
+    checked = {"gate_up": {"outputs": int(y_ref.size),
+                           "bad": int((~O.within_tolerance(y_timed["gate_up"], y_ref, a_ref)).sum())}}
+    del y_ref, a_ref
+    rng = np.random.default_rng(7)
+    for nm in ("qkv", "o_proj", "down"):
+        wn = layer[nm]
+        rows = np.sort(rng.choice(wn.shape[0], 256, replace=False))
+        xn = S.activations(16, wn.shape[1], S.x_seed(16, wn.shape[1]))
+        bad, _ = O.gemm_check(xn, wn[rows], y_timed[nm][:, rows])
+        checked[nm] = {"outputs": 16 * len(rows), "bad": int(bad)}
+    log(f"[bench] timed outputs against the oracle: {checked}")
+    assert all(c["bad"] == 0 for c in checked.values()), f"timed GEMM outputs fail the oracle check: {checked}"
     blas_threads, t1 = None, None
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
@@ -1159,7 +1316,88 @@ def cpu_baseline(layer, enc):
         "one_thread": None if t1 is None else {"s": round(t1, 3), "GBps": round(2 * n * k / t1 / 1e9, 3)},
         "oracle_encode": {"s": round(t_enc, 3), "GBps": round(2 * n * k / t_enc / 1e9, 3)},
         "oracle_decode_compare": {"s": round(t_cmp, 3), "GBps": round(2 * n * k / t_cmp / 1e9, 3)},
+        "timed_outputs_checked": checked,
     }
+
+
+def cpu_legs(n_layers, layer_range=None):
+    """The oracle on all host cores for the other workloads (BASELINE plan): the tiny case
+    (encode, decode-compare, GEMM at M=1), the tree-verify M sweep and the batched M on gate_up
+    and down (decode + FP64 GEMM, median of 3), the heavy-tail matrices (encode + decode + GEMM
+    at M=16), and the full model streamed one layer at a time (generate, encode, decode-compare,
+    FP64 GEMM at M=32 for each of the four matrices; the real total over n_layers layers, with
+    the generation time reported apart)."""
+    from oracle import w12_oracle as O
+
+    def med3(f):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    res = {"cores": len(os.sched_getaffinity(0)), "kind": "oracle", "unit": "s"}
+    try:
+        from threadpoolctl import threadpool_info
+        res["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        res["blas_threads"] = None
+    if layer_range is not None:
+        res["full_model"] = full_model_cpu(*layer_range)
+        return res
+    w = S.tiny_weights(0)
+    x = S.activations(1, w.shape[1], S.x_seed(1, w.shape[1]))
+    ref = O.encode(w)
+    res["tiny"] = {"encode": med3(lambda: O.encode(w)),
+                   "decode_compare": med3(lambda: np.array_equal(O.decode(ref), w)),
+                   "gemm_M1": med3(lambda: O.gemm_reference(x, O.decode(ref)))}
+    log(f"[cpu] tiny {res['tiny']}")
+    lay = S.layer(0, which=("gate_up", "down"))
+    for leg, ms in (("tree_sweep", S.TREE_M_SWEEP), ("batched", S.BATCHED_M)):
+        res[leg] = {}
+        for nm in ("gate_up", "down"):
+            wn = lay[nm]
+            refn = O.encode(wn)
+            for m in ms:
+                xm = S.activations(m, wn.shape[1], S.x_seed(m, wn.shape[1]))
+                res[leg][f"{nm}_M{m}"] = med3(lambda: O.gemm_reference(xm, O.decode(refn)))
+                log(f"[cpu] {leg} {nm} M={m}: {res[leg][f'{nm}_M{m}']:.2f} s")
+    del lay
+    res["heavy_tail"] = {}
+    for nm, seed in (("gate_up", 1000), ("down", 1001)):
+        n, k = S.LAYER_SHAPES[nm]
+        wh = S.heavy_tail_weights(seed, n, k)
+        xh = S.activations(16, k, S.x_seed(16, k))
+        t0 = time.perf_counter()
+        refh = O.encode(wh)
+        t_enc = time.perf_counter() - t0
+        res["heavy_tail"][nm] = {"escapes": int(refh.num_escapes), "encode": t_enc,
+                                 "gemm_M16": med3(lambda: O.gemm_reference(xh, O.decode(refh)))}
+        log(f"[cpu] heavy {nm} {res['heavy_tail'][nm]}")
+        del wh, refh
+    res["full_model"] = full_model_cpu(0, n_layers)
+    return res
+
+
+def full_model_cpu(first, end):
+    """The oracle over layers first..end-1 of the full model, one layer at a time."""
+    from oracle import w12_oracle as O
+    t_gen = t_work = 0.0
+    for seed in range(first, end):
+        t0 = time.perf_counter()
+        lay = S.layer(seed)
+        t_gen += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for nm in S.LAYER_ORDER:
+            wn = lay[nm]
+            r = O.encode(wn)
+            assert np.array_equal(O.decode(r), wn)
+            O.gemm_reference(S.activations(32, wn.shape[1], S.x_seed(32, wn.shape[1])), O.decode(r))
+        t_work += time.perf_counter() - t0
+        log(f"[cpu] full model layer {seed}: {t_work:.1f} s so far")
+    return {"layers": [first, end], "M": 32, "oracle_s": t_work, "generation_s": t_gen,
+            "what": "encode + decode-compare + FP64 GEMM of qkv, o_proj, gate_up, down per layer"}
 
 
 if __name__ == "__main__":

@@ -130,7 +130,7 @@ def _mut_subnormals_flushed(mp):
 
     def conv(w):
         v = orig(w)
-        return np.where((np.asarray(w, np.uint16) & 0x7F80) == 0, 0.0 * v, v)
+        return np.where((np.asarray(w, np.uint16) & 0x7F80) == 0, 0.0, v)
     mp.setattr(O, "bf16_to_f64", conv)
 
 
