@@ -196,6 +196,9 @@ def main():
                     help="sweep the plain streaming-read kernel (loads in flight x work-groups per CU) and exit")
     ap.add_argument("--probe-reps", type=int, default=3,
                     help="launches per case of --valu-probe (the counter summaries expect 3)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="with libw12_timeline.so (build --timeline): per-work-group timelines of the gate_up and "
+                         "down launches at M = 16 (and M = 1); writes the phase summary under profiles/")
     ap.add_argument("--r13-probe", action="store_true",
                     help="gate_up and down at M = 1..8, once through the wavefront GEMV (W12_GEMV_MAX_M=8) and once "
                          "through the 16-row MFMA tiles (W12_GEMV_MAX_M=0), --probe-reps launches each; prints the "
@@ -245,6 +248,9 @@ def main():
         rng = tuple(args.cpu_layers) if args.cpu_layers else None
         print(json.dumps(cpu_legs(args.model_layers, rng)))
         return
+    if args.timeline:
+        import lossless_bit_weight_encode_amd._lib as L
+        L.LIB_PATH = os.path.join(ROOT, "lossless_bit_weight_encode_amd", "libw12_timeline.so")
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.init()
     dev = torch.device("cuda:0")
@@ -255,6 +261,9 @@ def main():
         return
     if args.valu_probe:
         gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M, args.probe_reps)
+        return
+    if args.timeline:
+        timeline_leg(dev, stream, " ".join(["python3", "bench.py"] + sys.argv[1:]))
         return
     if args.r13_probe:
         gemm_probe(dev, stream, R13_MATS, R13_M, args.probe_reps, gemv_max=(8, 0))
@@ -624,6 +633,103 @@ def gemm_probe(dev, stream, mats, ms, reps=3, gemv_max=(None,)):
         os.environ.pop("W12_GEMV_MAX_M", None)
         del cs, e0
         torch.cuda.empty_cache()
+    print(json.dumps(res))
+
+
+TIMELINE_CASES = (("gate_up", 16), ("down", 16), ("gate_up", 1), ("o_proj", 16))
+
+
+def timeline_leg(dev, stream, command, launches=6):
+    """Per-work-group timelines (measurement build) of single GEMM launches on the layer
+    matrices, over >= 1 GiB of rotated encoded copies; summarised per phase into
+    profiles/gemm_M16_workgroup_timeline.md."""
+    import ctypes
+    import lossless_bit_weight_encode_amd._lib as L
+    lib = L.lib()
+    lib.w12_timeline_copy.restype = ctypes.c_int
+    lib.w12_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_uint64]
+    layer = S.layer(0, which=tuple(sorted({nm for nm, _ in TIMELINE_CASES})))
+    res = {}
+    P = lambda a, q: float(np.percentile(a, q))
+    for nm, m in TIMELINE_CASES:
+        n, k = S.LAYER_SHAPES[nm]
+        e0 = w12.encode(dev_bits(layer[nm]))
+        cs = [e0]
+        while sum(t.nbytes() for t in cs) < (1 << 30):
+            cs.append(clone_tensor(e0))
+        x = dev_bits(S.activations(m, k, S.x_seed(m, k)))
+        y = torch.empty(m, n, dtype=torch.float32, device=dev)
+        ws = w12.gemm_workspace(m, n, k)
+        plan = w12.gemm_plan(m, n, k)
+        G = plan["grid"]
+        for i in range(6):
+            w12.gemm(x, cs[i % len(cs)], y=y, ws=ws, stream=stream)
+        runs = []
+        for i in range(launches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            w12.gemm(x, cs[i % len(cs)], y=y, ws=ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            buf = np.zeros(G * 16, dtype=np.uint64)
+            assert lib.w12_timeline_copy(buf.ctypes.data, buf.nbytes) == 0
+            t = buf.reshape(G, 16).astype(np.int64)
+            rel = lambda c: (t[:, c] - t[:, 0].min()) / 100.0   # us
+            nseg = t[:, 13]
+            two = nseg >= 2
+            last_loop = np.where(two, rel(4), rel(2))
+            last_stores = np.where(two, rel(10), rel(7))
+            busy = last_loop - rel(1) - np.where(two, rel(3) - rel(2), 0.0)
+            first_wave = np.arange(G) < min(G, 256)
+            r = {"event_us": a.elapsed_time(b) * 1e3, "span_us": float(rel(11).max()),
+                 "start_skew_us": P(rel(0), 100), "prologue_us": P(rel(1) - rel(0), 50),
+                 "seg_end_wait_us": P(rel(5) - rel(2), 50), "reduce_us": P(rel(6) - rel(5), 50),
+                 "stores_us": P(rel(7) - rel(6), 50),
+                 "switch_us": P((rel(3) - rel(2))[two], 50) if two.any() else None,
+                 "fixup_us": P(rel(11) - last_stores, 50), "fixup_p90_us": P(rel(11) - last_stores, 90),
+                 "busy_p0_us": P(busy, 0), "busy_p50_us": P(busy, 50), "busy_p100_us": P(busy, 100),
+                 "busy_first_wave_us": float(busy[first_wave].mean()),
+                 "busy_second_wave_us": float(busy[~first_wave].mean()) if (~first_wave).any() else None,
+                 "end_p0_us": P(rel(11), 0), "end_p50_us": P(rel(11), 50), "end_p100_us": P(rel(11), 100),
+                 "segments": {int(a_): int(b_) for a_, b_ in zip(*np.unique(nseg, return_counts=True))}}
+            runs.append(r)
+        med = {key: (float(np.median([r[key] for r in runs])) if runs[0][key] is not None and
+                     not isinstance(runs[0][key], dict) else runs[0][key]) for key in runs[0]}
+        moved = alg_bytes(n, k, m, e0.num_escapes)
+        med["grid"] = G
+        med["alg_bytes"] = int(moved)
+        res[f"{nm}_M{m}"] = med
+        log(f"[timeline] {nm} M={m}: {json.dumps({k_: (round(v, 2) if isinstance(v, float) else v) for k_, v in med.items()})}")
+        del cs, e0
+        torch.cuda.empty_cache()
+    lines = ["# Per-work-group timeline of the streaming GEMM (MI355X)", "",
+             "Measurement build (`python -m lossless_bit_weight_encode_amd.build --timeline`, the same kernels with "
+             "thread 0 of every work-group stamping the 100 MHz real-time counter; include/w12_timeline.h), then:",
+             "", "```", command, "```", "",
+             f"Medians over {launches} launches (>= 1 GiB of rotated encoded copies). Per launch: the median over "
+             "work-groups of each phase; `busy` is a work-group's time in its step loops (switch excluded); "
+             "`first wave` / `second wave` are work-groups 0..255 / 256.. (dispatched breadth-first: the first "
+             "and the second work-group of each compute unit). Times in us from the earliest work-group start. "
+             "`event` brackets one launch on an idle GPU (the timeline is read back after every launch), so it "
+             "includes the idle-to-busy dispatch latency that back-to-back launches hide; `span` is first "
+             "work-group start to last work-group end.", "",
+             "| case | grid | event | span | start skew | prologue | seg end wait | reduce | stores | switch | "
+             "fixup (p50 / p90) | busy p0 / p50 / p100 | busy 1st / 2nd wave | end p0 / p50 / p100 |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    f2 = lambda v: "-" if v is None else f"{v:.2f}"
+    for key, r in res.items():
+        lines.append(f"| {key} | {r['grid']} | {f2(r['event_us'])} | {f2(r['span_us'])} | {f2(r['start_skew_us'])} | "
+                     f"{f2(r['prologue_us'])} | {f2(r['seg_end_wait_us'])} | {f2(r['reduce_us'])} | "
+                     f"{f2(r['stores_us'])} | {f2(r['switch_us'])} | {f2(r['fixup_us'])} / {f2(r['fixup_p90_us'])} | "
+                     f"{f2(r['busy_p0_us'])} / {f2(r['busy_p50_us'])} / {f2(r['busy_p100_us'])} | "
+                     f"{f2(r['busy_first_wave_us'])} / {f2(r['busy_second_wave_us'])} | "
+                     f"{f2(r['end_p0_us'])} / {f2(r['end_p50_us'])} / {f2(r['end_p100_us'])} |")
+    # written under profiles/ and, when the run has one, under gpurun_out/ as well
+    for d in ("profiles", "gpurun_out"):
+        if os.path.isdir(os.path.join(ROOT, d)):
+            with open(os.path.join(ROOT, d, "gemm_M16_workgroup_timeline.md"), "w") as f:
+                f.write("\n".join(lines) + "\n")
     print(json.dumps(res))
 
 

@@ -365,6 +365,17 @@ double w12_bits_per_weight(int32_t N, int32_t K, int64_t E) {
   return (1.5 * nk + (double)N + 4.0 * ((double)N + 1.0) + 4.0 * (double)E) * 8.0 / nk;
 }
 
+#ifdef W12_TIMELINE
+#include "w12_timeline.h"
+int w12_timeline_copy(void* host, uint64_t bytes) {
+  if (!host) return fail(W12_ERR_INVALID_ARG, "host is NULL");
+  if (bytes == 0 || bytes > (uint64_t)w12::kMaxGrid * 16 * 8)
+    return fail(W12_ERR_INVALID_ARG, "bytes=%llu outside 1..%llu", (unsigned long long)bytes,
+                (unsigned long long)w12::kMaxGrid * 16 * 8);
+  return hip_status(w12::timeline_copy(host, bytes), "timeline_copy");
+}
+#endif
+
 uint64_t w12_tensor_bytes(int32_t N, int32_t K, int64_t E) {
   if (N < 1 || K < 1 || E < 0) return 0;
   const uint64_t nk = (uint64_t)N * (uint64_t)K;

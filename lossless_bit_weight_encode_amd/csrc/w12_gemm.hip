@@ -513,6 +513,35 @@ struct MfmaPath {
 // invalidate the whole L2 of the XCD instead.
 // ------------------------------------------------------------------------------------------
 
+// ------------------------------------------------------------------------------------------
+// Measurement build only (-DW12_TIMELINE, libw12_timeline.so): thread 0 of every work-group
+// stamps the real-time counter (100 MHz) at fixed points of the streaming kernel into slots
+// of w12_timeline[work-group][16]; w12_timeline_copy reads them back.  Slots: 0 start,
+// 1 prologue done, 2 / 4 first / second segment's step loop done (wave 0), 3 switch done,
+// 5 / 8 the segment's last stage waited for, 6 / 9 cross-wave reduction done, 7 / 10 partial
+// or Y stores issued, 11 end, 12 compute-unit id, 13 segments, 14 fixup: own stores complete,
+// 15 fixup: arrival counters updated.  The normal build compiles none of this.
+// ------------------------------------------------------------------------------------------
+#ifdef W12_TIMELINE
+__device__ unsigned long long w12_timeline[kMaxGrid * 16];
+#define W12_TL(slot)                                                                           \
+  do {                                                                                         \
+    if (threadIdx.x == 0)                                                                      \
+      w12_timeline[(size_t)blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime();       \
+  } while (0)
+#define W12_TL_VAL(slot, v)                                                                    \
+  do {                                                                                         \
+    if (threadIdx.x == 0) w12_timeline[(size_t)blockIdx.x * 16 + (slot)] = (v);               \
+  } while (0)
+#else
+#define W12_TL(slot) \
+  do {               \
+  } while (0)
+#define W12_TL_VAL(slot, v) \
+  do {                      \
+  } while (0)
+#endif
+
 // Stream-K bookkeeping: work-group w owns units [ubeg(w), ubeg(w+1)).
 __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w * g.units / g.G; }
 
@@ -717,6 +746,9 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   __shared__ uint32_t s_flag[kMaxPend];
   __shared__ uint32_t s_pend[kMaxPend];   // tiles of this work-group's partial segments
   __shared__ uint32_t s_pendg[kMaxPend];  // and their products
+  W12_TL(0);
+  int tl_seg = 0;   // segments done (the timeline build's slot index)
+  (void)tl_seg;
   const int wave = wave_id();
   // units, G and P are launch-wide: the same in every member of a group
   const int64_t u_first = ubeg(ga.g[0], blockIdx.x);
@@ -774,6 +806,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   issue_slice(re, s0, &slices[0][0], wave);
   wait_vmcnt<0>();
   barrier();
+  W12_TL(1);
 
   int sb = 0;   // slice buffer of the current segment
   bool in_lds = (s1 - s0) <= (uint32_t)kSliceEntries;
@@ -794,6 +827,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   auto flush_pending = [&]() {
     wait_vm_all();   // this work-group's partial stores are complete
     __syncthreads();
+    W12_TL(14);
     if (threadIdx.x < (unsigned)npend) {
       const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[threadIdx.x] : 0];
       const int64_t tile = s_pend[threadIdx.x];
@@ -805,6 +839,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       s_flag[threadIdx.x] = (prev == nsegs - 1) ? 1u : 0u;
     }
     __syncthreads();
+    W12_TL(15);
     for (int p = 0; p < npend; ++p) {
       if (!s_flag[p]) continue;
       const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[p] : 0];
@@ -943,6 +978,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     }
 
     // ---- segment end ----
+    if (tl_seg < 2) W12_TL(2 + 2 * tl_seg);
     if (has_next && !next_sliced) {   // a one-step segment
       slice_range(ng, nrg, nse, ns0, ns1);
       issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
@@ -962,12 +998,14 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     } else {
       wait_vmcnt<0>();
     }
+    if (tl_seg < 2) W12_TL(5 + 3 * tl_seg);
     // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
       if (wave == w) Path::to_red(acc, red_addr, w == 0);
       wait_lgkm();
       barrier();
     }
+    if (tl_seg < 2) W12_TL(6 + 3 * tl_seg);
     const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
     const int m0 = cur.m0 * MROWS;
     // partial slot: the work-group's first or last segment
@@ -1002,10 +1040,13 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       }
       ++npend;
     }
+    if (tl_seg < 2) W12_TL(7 + 3 * tl_seg);
+    ++tl_seg;
     if (!has_next) break;
     if constexpr (!Path::kXInLds) Path::load_x(ng, nr.x, nx.m0 * MROWS, nx.sl.c0, nx.sl.c0 < nx.sl.c_end, xa0, xb0);
     wait_lgkm();
     barrier();   // red is free again; the next slice is visible to every wave
+    if (tl_seg == 1) W12_TL(3);
     // switch to the next segment
     cur = nx;
     sb ^= 1;
@@ -1021,6 +1062,9 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
 
   // ---- deferred split-K fixups ----
   if (npend) flush_pending();
+  W12_TL(11);
+  W12_TL_VAL(12, (unsigned long long)__smid());
+  W12_TL_VAL(13, (unsigned long long)tl_seg);
 }
 
 template <class Path, bool kQ>
@@ -1380,5 +1424,11 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
   dispatch(p, ga, qpass, stream);
   return hipGetLastError();
 }
+
+#ifdef W12_TIMELINE
+hipError_t timeline_copy(void* host, uint64_t bytes) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(w12_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 }  // namespace w12

@@ -68,6 +68,11 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
 constexpr uint64_t kScratchBytes = uint64_t(32) << 20;
 hipError_t scratch_workspace(void** ws, hipStream_t stream);
 
+#ifdef W12_TIMELINE
+// Measurement build: the per-work-group timeline of the last streaming GEMM (w12_gemm.hip).
+hipError_t timeline_copy(void* host, uint64_t bytes);
+#endif
+
 // Measurement aid: a plain streaming read of `bytes` bytes (w12_probe.hip).
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, int32_t loads_per_lane, int64_t grid, uint32_t* sink,
                              hipStream_t stream);
