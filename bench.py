@@ -199,6 +199,15 @@ def main():
     ap.add_argument("--timeline", action="store_true",
                     help="with libw12_timeline.so (build --timeline): per-work-group timelines of the gate_up and "
                          "down launches at M = 16 (and M = 1); writes the phase summary under profiles/")
+    ap.add_argument("--sweep-probe", action="store_true",
+                    help="gate_up and down at M = 1..64 (the default paths), --probe-reps launches each, for a "
+                         "kernel trace (--summarize-sweep-trace)")
+    ap.add_argument("--read-trace-probe", action="store_true",
+                    help="the plain streaming read at the matrices' sizes and 1 GiB (best launch shape), for a "
+                         "kernel trace (--summarize-read-trace)")
+    ap.add_argument("--summarize-read-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace run of --read-trace-probe into the read-ceiling summary "
+                         "under profiles/")
     ap.add_argument("--r13-probe", action="store_true",
                     help="gate_up and down at M = 1..8, once through the wavefront GEMV (W12_GEMV_MAX_M=8) and once "
                          "through the 16-row MFMA tiles (W12_GEMV_MAX_M=0), --probe-reps launches each; prints the "
@@ -215,6 +224,9 @@ def main():
         return
     if args.summarize_r13_trace:
         summarize_r13_trace(*args.summarize_r13_trace)
+        return
+    if args.summarize_read_trace:
+        summarize_read_trace(*args.summarize_read_trace)
         return
     if args.summarize_encode_lds:
         summarize_encode_lds(*args.summarize_encode_lds)
@@ -261,6 +273,13 @@ def main():
         return
     if args.valu_probe:
         gemm_probe(dev, stream, VALU_PROBE_MATS, VALU_PROBE_M, args.probe_reps)
+        return
+    if args.sweep_probe:
+        gemm_probe(dev, stream, ("gate_up", "down"), VALU_PROBE_M, args.probe_reps)
+        return
+    if args.read_trace_probe:
+        res = read_ceiling(dev, stream, [READ_BEST])
+        print(json.dumps({"sizes": READ_SIZES, "variant": list(READ_BEST), "warmup": 3, "reps": 20, "read": res}))
         return
     if args.timeline:
         timeline_leg(dev, stream, " ".join(["python3", "bench.py"] + sys.argv[1:]))
@@ -706,7 +725,7 @@ def timeline_leg(dev, stream, command, launches=6):
     lines = ["# Per-work-group timeline of the streaming GEMM (MI355X)", "",
              "Measurement build (`python -m lossless_bit_weight_encode_amd.build --timeline`, the same kernels with "
              "thread 0 of every work-group stamping the 100 MHz real-time counter; include/w12_timeline.h), then:",
-             "", "```", command, "```", "",
+             "", "```", command, "```", "", f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
              f"Medians over {launches} launches (>= 1 GiB of rotated encoded copies). Per launch: the median over "
              "work-groups of each phase; `busy` is a work-group's time in its step loops (switch excluded); "
              "`first wave` / `second wave` are work-groups 0..255 / 256.. (dispatched breadth-first: the first "
@@ -731,6 +750,41 @@ def timeline_leg(dev, stream, command, launches=6):
             with open(os.path.join(ROOT, d, "gemm_M16_workgroup_timeline.md"), "w") as f:
                 f.write("\n".join(lines) + "\n")
     print(json.dumps(res))
+
+
+def summarize_read_trace(trace_csv, probe_json, command):
+    """rocprofv3 kernel durations of the --read-trace-probe launches (warm-up launches dropped):
+    the plain streaming read's bytes per second at each size, the practical HBM read ceiling."""
+    import csv
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    rd = [r for r in trace if "k_read_probe" in r["Kernel_Name"]]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    u, g = probe["variant"]
+    lines = ["# Plain streaming read (practical HBM read ceiling), MI355X", "",
+             "Command (run from the repository root):", "", "```", command, "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
+             f"`w12_read_probe`: {g} work-groups of 256 threads per compute unit, each reading a contiguous share "
+             f"with 16-byte loads, {u} loads in flight per lane; every launch reads a different part of a 2 GiB "
+             "buffer (so the 256 MB Infinity Cache cannot serve it). Kernel trace durations over the timed "
+             "launches of each size.", "",
+             "| size | bytes | launches | median us | min us | GB/s (median) | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    i = 0
+    for name, nb in probe["sizes"].items():
+        nb = nb // 256 * 256
+        rows = rd[i + probe["warmup"]:i + probe["warmup"] + probe["reps"]]
+        i += probe["warmup"] + probe["reps"]
+        d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
+        med = float(np.median(d))
+        lines.append(f"| {name} | {nb} | {len(d)} | {med:.2f} | {d.min():.2f} | {nb / med / 1e3:.0f} | "
+                     f"{nb / med / 1e3 / HBM_PEAK_GBPS:.3f} |")
+    assert i == len(rd), f"{len(rd) - i} read launches in the trace are not in the probe"
+    path = os.path.join(ROOT, "profiles", "read_probe_ceiling_kernel_trace.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 R13_MATS = ("gate_up", "down")
@@ -762,6 +816,7 @@ def summarize_r13_trace(trace_csv, probe_json, command):
     assert i == len(gemm), f"{len(gemm) - i} GEMM launches in the trace are not in the probe"
     lines = ["# Wavefront GEMV against 16-row MFMA tiles at M = 1..8 (gate_up 34816 x 5120, down 5120 x 17408), "
              "MI355X", "", "Command (run from the repository root):", "", "```", command, "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
              "Kernel trace durations (median and mean over the launches of each case, the first dropped; three "
              "rotating encoded copies). `GemvPath<M>` is the FP32 dot2 wavefront GEMV (W12_GEMV_MAX_M=8), "
              "`MfmaPath<1>` the bf16 MFMA 16-row tile (W12_GEMV_MAX_M=0). Fraction = algorithmic bytes of the "
@@ -948,15 +1003,18 @@ def summarize_sweep_trace(trace_csv, probe_json, command):
     gemm = [r for r in trace if "k_gemm" in r["Kernel_Name"]]
     with open(probe_json) as f:
         probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
-    lines = ["# W12 GEMM kernel times over the M sweep: gate_up 34816 x 5120, MI355X", "",
+    mats = [nm for nm in S.LAYER_ORDER if any(key.startswith(nm + "_M") for key in probe)]
+    lines = ["# W12 GEMM kernel times over the M sweep: " +
+             ", ".join(f"{nm} {S.LAYER_SHAPES[nm][0]} x {S.LAYER_SHAPES[nm][1]}" for nm in mats) + ", MI355X", "",
              "Command (run from the repository root):", "", "```", command, "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
              "Kernel trace durations; each M runs R launches on three rotating encoded copies (the first is "
              "dropped).", "Moved bytes are the algorithmic bytes of the launch (records, bases, pointers, "
              "escapes, X, Y).", "",
-             "| M | kernel | launches | avg us | median us | min us | weight-GB/s (median) | "
-             "moved GB/s (median) | of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+             "| matrix | M | kernel | launches | avg us | median us | min us | weight-GB/s (median) | "
+             "moved GB/s (median) | of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
     i = 0
-    for nm in VALU_PROBE_MATS:
+    for nm in mats:
         n, k = S.LAYER_SHAPES[nm]
         for m in VALU_PROBE_M:
             info = probe[f"{nm}_M{m}"]
@@ -966,10 +1024,11 @@ def summarize_sweep_trace(trace_csv, probe_json, command):
             d = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows])
             med = float(np.median(d))
             moved = alg_bytes(n, k, m, info["escapes"])
-            lines.append(f"| {m} | `{info['kernel']}` | {len(d)} | {d.mean():.2f} | {med:.2f} | {d.min():.2f} | "
+            lines.append(f"| {nm} | {m} | `{info['kernel']}` | {len(d)} | {d.mean():.2f} | {med:.2f} | {d.min():.2f} | "
                          f"{2 * n * k / med / 1e3:.0f} | {moved / med / 1e3:.0f} | "
                          f"{moved / med / 1e3 / HBM_PEAK_GBPS:.3f} |")
-    path = os.path.join(ROOT, "profiles", "gemm_gate_up_M1_M64_kernel_trace.md")
+    assert i == len(gemm), f"{len(gemm) - i} GEMM launches in the trace are not in the probe"
+    path = os.path.join(ROOT, "profiles", "gemm_" + "_".join(mats) + "_M1_M64_kernel_trace.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -1179,6 +1238,18 @@ def traffic_from_profile(alg):
     return {"traffic": d["hbm_bytes_per_launch"], "traffic_over_alg": round(d["hbm_bytes_per_launch"] / alg, 4)}
 
 
+def source_stamp() -> str:
+    """SHA-256 (first 16 hex digits) of the kernel sources and headers, for the summaries under
+    profiles/: a summary whose stamp differs from the tree's predates a kernel change."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_bit_weight_encode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def summarize_trace(stats_csv, trace_csv, command):
     """Kernel-time summary of a profiled --only-layer run: rocprofv3's per-kernel stats, plus the
     GEMM durations split by matrix (the four layer GEMMs share one kernel name and are launched
@@ -1191,6 +1262,7 @@ def summarize_trace(stats_csv, trace_csv, command):
     gemm = [r for r in trace if "k_gemm" in r["Kernel_Name"]]
     lines = ["# W12 GEMM kernel times: one dense decoder layer (hidden 5120), M=16, MI355X", "",
              "Command (run from the repository root):", "", "```", command, "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
              "## rocprofv3 --stats (all kernels of the run)", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in stats:
