@@ -148,6 +148,9 @@ def main():
                     help="only the oracle on the host cores, for the tiny case, the tree-verify M sweep, the batched "
                          "M and heavy-tail matrices, and the full model streamed one layer at a time (no GPU; "
                          "several minutes); prints one JSON line")
+    ap.add_argument("--summarize-cpu-legs", nargs="+", metavar="JSON",
+                    help="turn the JSON lines of --cpu-legs runs (the other legs, and the full model in parts) into "
+                         "profiles/cpu_oracle_legs.md")
     ap.add_argument("--cpu-layers", nargs=2, type=int, metavar=("FIRST", "END"),
                     help="with --cpu-legs: only the full-model leg, over layers FIRST..END-1 (so the whole model can "
                          "be timed in parts whose totals add up)")
@@ -224,6 +227,9 @@ def main():
         return
     if args.summarize_r13_trace:
         summarize_r13_trace(*args.summarize_r13_trace)
+        return
+    if args.summarize_cpu_legs:
+        summarize_cpu_legs(args.summarize_cpu_legs)
         return
     if args.summarize_read_trace:
         summarize_read_trace(*args.summarize_read_trace)
@@ -1556,6 +1562,54 @@ def cpu_legs(n_layers, layer_range=None):
         del wh, refh
     res["full_model"] = full_model_cpu(0, n_layers)
     return res
+
+
+def summarize_cpu_legs(paths):
+    """profiles/cpu_oracle_legs.md from --cpu-legs JSON lines: the legs of one run, and the full
+    model summed over runs that cover disjoint layer ranges (all 64 layers between them)."""
+    runs = []
+    for p in paths:
+        with open(p) as f:
+            runs.append(json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1]))
+    legs = next(r for r in runs if "tree_sweep" in r)
+    parts = [r["full_model"] for r in runs if r.get("full_model", {}).get("layers", [0, 0])[1] >
+             r.get("full_model", {}).get("layers", [0, 0])[0]]
+    layers = sorted(i for a, b in (p["layers"] for p in parts) for i in range(a, b))
+    assert len(layers) == len(set(layers)), "the layer ranges overlap"
+    cores = {r["cores"] for r in runs}
+    gbps = lambda nm, t: 2 * S.LAYER_SHAPES[nm][0] * S.LAYER_SHAPES[nm][1] / t / 1e9
+    lines = ["# The CPU oracle on the other workloads (host cores of the MI355X box)", "",
+             "Commands (run from the repository root; the full model in two parts whose layer ranges cover 0..63):",
+             "", "```", "python3 bench.py --cpu-legs --model-layers 0", "python3 bench.py --cpu-legs --cpu-layers 0 16",
+             "python3 bench.py --cpu-legs --cpu-layers 16 64",
+             "python3 bench.py --summarize-cpu-legs <the three JSON outputs>", "```", "",
+             f"The oracle as it stands (numpy, FP64 GEMM through the BLAS), {sorted(cores)} cores, "
+             f"{legs.get('blas_threads')} BLAS threads. GEMM legs: decode + FP64 GEMM (+ the sum of |x w|), median "
+             "of 3; GB/s = BF16 bytes of W (2NK) per second. A reported baseline, not a target.", "",
+             "| leg | case | seconds | GB/s (2NK / t) |", "|---|---|---|---|"]
+    t = legs["tiny"]
+    lines.append(f"| tiny 256x512 | encode / decode-compare / GEMM M=1 | {t['encode']:.4f} / "
+                 f"{t['decode_compare']:.4f} / {t['gemm_M1']:.4f} | - |")
+    for leg in ("tree_sweep", "batched"):
+        for key, v in legs[leg].items():
+            nm = key.split("_M")[0]
+            lines.append(f"| {leg} | {key} | {v:.3f} | {gbps(nm, v):.3f} |")
+    for nm, v in legs["heavy_tail"].items():
+        lines.append(f"| heavy_tail | {nm} (E = {v['escapes']}): encode / GEMM M=16 | {v['encode']:.3f} / "
+                     f"{v['gemm_M16']:.3f} | {gbps(nm, v['gemm_M16']):.3f} (GEMM) |")
+    if layers:
+        tot = sum(p["oracle_s"] for p in parts)
+        gen = sum(p["generation_s"] for p in parts)
+        wb = len(layers) * sum(2 * n * k for n, k in S.LAYER_SHAPES.values())
+        lines += ["", f"Full model, one layer at a time: layers {layers[0]}..{layers[-1]} "
+                      f"({len(layers)} layers{'' if layers == list(range(len(layers))) else ', with gaps'}), per layer "
+                      "the oracle's encode, decode-compare and FP64 GEMM at M = 32 of qkv, o_proj, gate_up and down: "
+                      f"**{tot:.1f} s** in all ({wb / tot / 1e9:.3f} GB/s of BF16 weights), plus {gen:.1f} s to draw "
+                      "the layers (not counted)."]
+    path = os.path.join(ROOT, "profiles", "cpu_oracle_legs.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def full_model_cpu(first, end):

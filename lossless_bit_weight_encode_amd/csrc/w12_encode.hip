@@ -1,11 +1,12 @@
 // W12 encode kernels: per-channel window choice, escape-count scan, record emission.
 //
-// SpecPilot summary page, method bullet of section 4.1: each weight becomes sign | 4-bit
-// exponent offset inside a 16-binade window per output channel | 7 mantissa bits, and
-// out-of-window weights, zeros and denormals go to an exact escape list.  News article
-// "(1) W12": BF16 exponents cluster within an output channel, which is what makes a
-// per-channel window pay.  The window base b of a channel is the smallest b in 1..239 that
-// maximises the number of weights with exponent field in [b, b+15].
+// The record (SpecPilot summary page, method bullet of section 4.1) keeps a weight's sign, its
+// exponent as a 4-bit offset from the channel's window base (a window of 16 binades) and the
+// top 7 mantissa bits; the weights a record cannot hold (exponent outside the window, zero,
+// subnormal) go to an exact side list.  Per the news article, part "(1) W12", the exponents of
+// one output channel sit close together, which is what makes a per-channel window pay.  The
+// window base b of a channel is the smallest b in 1..239 that maximises the number of weights
+// with exponent field in [b, b+15].
 #include "w12_device.h"
 #include "w12_gemm_common.h"
 #include "w12_kernels.h"
