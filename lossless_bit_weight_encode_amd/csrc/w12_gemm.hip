@@ -324,6 +324,7 @@ struct GemvPath {
   static constexpr int kMRows = M;
   static constexpr int kWavesPerEU = 2;   // register budget: two work-groups per CU
   static constexpr bool kXInLds = true;
+  static constexpr int kWStages = 2;      // W ring stages
   static constexpr int kVmemPerStage = 7;   // 6 W DMA + 1 X DMA
   typedef float Acc;
   static constexpr int kAcc = M;
@@ -411,6 +412,10 @@ struct MfmaPath {
   // case: 5-7% faster than register X); 32-row tiles keep X in registers, which keeps two
   // work-groups per CU (with X in LDS they would need 98 KB each)
   static constexpr bool kXInLds = MB != 2;
+  // W ring stages: three for the 64-row tiles (one work-group per CU, so LDS has room for a
+  // third), keeping two W stages in flight per CU as two work-groups of the smaller tiles do
+  // (measured: 4-6% faster at M = 63 / 64; no gain for the 48-row tiles, which keep two)
+  static constexpr int kWStages = MB == 4 ? 3 : 2;
   static constexpr int kVmemPerStage = 6 + 2 * MB;   // 6 W DMA + 2 MB X loads
   typedef f32x4 Acc;
   static constexpr int kAcc = MB;
@@ -711,6 +716,22 @@ __device__ __forceinline__ void seg_setup(const GemmArgs& g, int gi, int64_t u, 
 // At most `pend` vector-memory instructions may remain outstanding.  pend counts loads only
 // (a stage: V, escape metadata: 2 kRB, the escape slice: 1); any other value waits for
 // everything.  Leaving an instruction out of the count only makes the wait longer.
+// The three-stage loop's waits: pend is a sum of (VW + VX) for the next stage's X and W, VW for
+// the stage after it, 2 kRB escape-metadata loads and 1 slice DMA.
+template <int VW, int VX>
+__device__ __forceinline__ void wait_pending3(int pend) {
+  constexpr int A = VW + VX, B = VW, E = 2 * kRB;
+  if (pend == A + B) wait_vmcnt<A + B>();
+  else if (pend == A + B + E) wait_vmcnt<A + B + E>();
+  else if (pend == A + B + 1) wait_vmcnt<A + B + 1>();
+  else if (pend == A) wait_vmcnt<A>();
+  else if (pend == A + E) wait_vmcnt<A + E>();
+  else if (pend == A + 1) wait_vmcnt<A + 1>();
+  else if (pend == E) wait_vmcnt<E>();
+  else if (pend == 1) wait_vmcnt<1>();
+  else wait_vmcnt<0>();
+}
+
 template <int V>
 __device__ __forceinline__ void wait_pending(int pend) {
   constexpr int E = 2 * kRB;
@@ -739,10 +760,20 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   constexpr int TILE_ELEMS = ROWS * MROWS;
   constexpr int ET = (TILE_ELEMS + kThreads - 1) / kThreads;   // output elements per thread
   typedef typename Path::XStage XStage;
+  // Three W stages (64-row tiles): W runs two steps ahead of the stage being computed,
+  // X one.  The reduction buffer then shares the second X slot, which is idle whenever red is
+  // in use (a segment's end: the next segment's X stage 0 goes to the first slot), so the third
+  // W stage fits in LDS.
+  constexpr bool kW3 = Path::kWStages == 3;
+  static_assert(!kW3 || Path::kXInLds, "three W stages need X in LDS");
+  constexpr int VW = kQ ? 4 : 6;   // W DMAs of a stage (the Q pass reads no lo plane)
+  constexpr int VX = V - VW;       // X DMAs of a stage
   __shared__ RingStage<RB> ring0, ring1;
+  __shared__ typename std::conditional<kW3, RingStage<RB>, char>::type ring2;
   __shared__ XStage xring0, xring1;
   __shared__ uint4 slices[2][kSliceEntries / 4];
-  __shared__ float red[TILE_ELEMS];
+  __shared__ float red_buf[kW3 ? 1 : TILE_ELEMS];
+  static_assert(!kW3 || sizeof(XStage) >= TILE_ELEMS * sizeof(float), "red must fit the second X slot");
   __shared__ uint32_t s_flag[kMaxPend];
   __shared__ uint32_t s_pend[kMaxPend];   // tiles of this work-group's partial segments
   __shared__ uint32_t s_pendg[kMaxPend];  // and their products
@@ -773,13 +804,18 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       lo0[i] = make_uint4(0, 0, 0, 0);
       lo1[i] = make_uint4(0, 0, 0, 0);
     }
+    if constexpr (kW3) {
+      uint4* lo2 = &ring2.lo[0][0];
+      for (int i = threadIdx.x; i < kWaves * RB * 32; i += kThreads) lo2[i] = make_uint4(0, 0, 0, 0);
+    }
   }
 
-  uint32_t ah0, al0, ah1, al1;
+  uint32_t ah0, al0, ah1, al1, ah2 = 0, al2 = 0;
   ring_addr<RB>(&ring0, wave, ah0, al0);
   ring_addr<RB>(&ring1, wave, ah1, al1);
+  if constexpr (kW3) ring_addr<RB>(&ring2, wave, ah2, al2);
   const uint32_t slice_addr0 = lds_off(&slices[0][0]), slice_addr1 = lds_off(&slices[1][0]);
-  const uint32_t red_addr = lds_off(&red[0]);
+  const uint32_t red_addr = kW3 ? lds_off(&xring1) : lds_off(&red_buf[0]);
 
   // ---- prologue: the first segment's escape metadata and stage 0 (interleaved mapping
   // assumed), then the escape slice ----
@@ -804,7 +840,17 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     issue_stage0();
   }
   issue_slice(re, s0, &slices[0][0], wave);
-  wait_vmcnt<0>();
+  if constexpr (kW3) {
+    // and W stage 1, which stays in flight through the barrier
+    if (cur.sl.iters > 1) {
+      issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, 1, &ring1, wave);
+      wait_vmcnt<VW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  } else {
+    wait_vmcnt<0>();
+  }
   barrier();
   W12_TL(1);
 
@@ -920,8 +966,9 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     const uint32_t sl_addr = sb ? slice_addr1 : slice_addr0;
 
     // stage j is complete once at most `pend` newer vector-memory instructions remain
+    // (pend < 0: the caller has waited)
     auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
-      wait_pending<V>(pend);
+      if (pend >= 0) wait_pending<V>(pend);
       static_assert(RB == 4, "ring reads are written for 4 row blocks");
       uint4 h[RB];
       uint2 l[RB];
@@ -937,6 +984,43 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
         Path::mac(d, xa, xb, acc[rb]);
       }
     };
+    if constexpr (kW3) {
+      // stage j: W in ring j mod 3 (issued two steps ahead), X in xring j mod 2 (one step ahead)
+      uint32_t wa = ah0, wl = al0, wa1 = ah1, wl1 = al1, wa2 = ah2, wl2 = al2;   // W slots of stages j, j+1, j+2
+      for (uint32_t j = 0; j < iters; ++j) {
+        int pend = 0;
+        if (has_next && j == 0) {   // the next segment's esc_ptr pairs and bases
+          load_seg_esc(ng, nr.p, nr.base, nrg, nse);
+          pend += 2 * RB;
+        }
+        if (has_next && j == 1) {   // the next segment's escape slice (the compiler waits for the pairs)
+          slice_range(ng, nrg, nse, ns0, ns1);
+          issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
+          next_sliced = true;
+          pend += 1;
+        }
+        if (j + 1 < iters) {
+          Path::issue_x(g, rx, cur.xc0, cur.xc_end, cur.sl.stride, cur.m0 * MROWS, j + 1, (j & 1) ? &xring0 : &xring1,
+                        wave);
+          pend += VX + VW;   // X of stage j + 1, and its W (issued a step earlier)
+        }
+        if (j + 2 < iters) {
+          const uint32_t sw = (j + 2) % 3;
+          issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, j + 2, sw == 0 ? &ring0 : (sw == 1 ? &ring1 : &ring2), wave);
+          pend += VW;
+        }
+        // stages j complete once at most `pend` newer vector-memory instructions remain
+        wait_pending3<VW, VX>(pend);
+        compute(wa, wl, (j & 1) ? &xring1 : &xring0, xa0, xb0, j, -1);
+        const uint32_t ta = wa, tl = wl;
+        wa = wa1;
+        wl = wl1;
+        wa1 = wa2;
+        wl1 = wl2;
+        wa2 = ta;
+        wl2 = tl;
+      }
+    } else {
     for (uint32_t j = 0; j < iters; j += 2) {
       // even step: stage j in ring0
       const bool more1 = j + 1 < iters;
@@ -976,6 +1060,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       }
       compute(ah1, al1, &xring1, xa1, xb1, j + 1, pend);
     }
+    }
 
     // ---- segment end ----
     if (tl_seg < 2) W12_TL(2 + 2 * tl_seg);
@@ -994,11 +1079,24 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
       issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 0, &ring0, wave);
       if constexpr (Path::kXInLds) Path::issue_x(ng, nr.x, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
-      wait_vmcnt<V0>();   // this wave's part of the next slice has landed (it precedes stage 0)
+      if constexpr (kW3) {
+        // and its W stage 1 (the slot of red, the second X slot, is not written before the switch)
+        if (nx.sl.iters > 1) {
+          issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 1, &ring1, wave);
+          wait_vmcnt<2 * VW + VX>();   // the next slice has landed (it precedes those stages)
+        } else {
+          wait_vmcnt<VW + VX>();
+        }
+      } else {
+        wait_vmcnt<V0>();   // this wave's part of the next slice has landed (it precedes stage 0)
+      }
     } else {
       wait_vmcnt<0>();
     }
     if (tl_seg < 2) W12_TL(5 + 3 * tl_seg);
+    // red spans every wave's part of the second X slot: no wave writes it before all have read
+    // their last X stage
+    if constexpr (kW3) barrier();
     // waves add their partial tiles into red in wave order
     for (int w = 0; w < kWaves; ++w) {
       if (wave == w) Path::to_red(acc, red_addr, w == 0);
