@@ -218,12 +218,22 @@ def main():
     ap.add_argument("--summarize-r13-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
                     help="turn a rocprofv3 --kernel-trace run of --r13-probe into the GEMV-vs-MFMA summary under "
                          "profiles/")
+    ap.add_argument("--encode-probe", action="store_true",
+                    help="encode the layer's four matrices and the two heavy-tail matrices with each emit form "
+                         "(auto, blocks, rows), --probe-reps encodes each, for a kernel trace "
+                         "(--summarize-encode-trace)")
+    ap.add_argument("--summarize-encode-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
+                    help="turn a rocprofv3 --kernel-trace run of --encode-probe into the encode kernel-time "
+                         "summary under profiles/")
     ap.add_argument("--summarize-sweep-trace", nargs=3, metavar=("TRACE_CSV", "PROBE_JSON", "COMMAND"),
                     help="turn a rocprofv3 --kernel-trace run of --valu-probe into the per-M kernel-time summary "
                          "under profiles/")
     args = ap.parse_args()
     if args.summarize_sweep_trace:
         summarize_sweep_trace(*args.summarize_sweep_trace)
+        return
+    if args.summarize_encode_trace:
+        summarize_encode_trace(*args.summarize_encode_trace)
         return
     if args.summarize_r13_trace:
         summarize_r13_trace(*args.summarize_r13_trace)
@@ -282,6 +292,9 @@ def main():
         return
     if args.sweep_probe:
         gemm_probe(dev, stream, ("gate_up", "down"), VALU_PROBE_M, args.probe_reps)
+        return
+    if args.encode_probe:
+        encode_probe(dev, stream, args.probe_reps)
         return
     if args.read_trace_probe:
         res = read_ceiling(dev, stream, [READ_BEST])
@@ -659,6 +672,117 @@ def gemm_probe(dev, stream, mats, ms, reps=3, gemv_max=(None,)):
         del cs, e0
         torch.cuda.empty_cache()
     print(json.dumps(res))
+
+
+
+
+def encode_cases():
+    """(label, n, k, BF16 bits) of the encode probe: layer 0's four matrices, then the heavy-tail
+    gate_up and down (seeds 1000 / 1001, as in the parity tests)."""
+    layer = S.layer(0)
+    for nm in S.LAYER_ORDER:
+        yield nm, layer[nm]
+    for nm, seed in (("gate_up", 1000), ("down", 1001)):
+        n, k = S.LAYER_SHAPES[nm]
+        yield f"heavy_{nm}", S.heavy_tail_weights(seed, n, k)
+
+
+def encode_probe(dev, stream, reps=3):
+    """Each matrix of encode_cases: one checked encode, then ``reps`` count passes (count + scan)
+    back to back, ``reps`` emits back to back (the kernels in steady state), and ``reps`` whole
+    encodes, each with its read-back of E (timed with events: the load-time cost).  Prints the
+    case order, escape counts and the whole-encode times as JSON; the kernel times come from the
+    trace."""
+    res = []
+    for label, bits in encode_cases():
+        n, k = bits.shape
+        w = dev_bits(bits)
+        t = w12.encode(w, stream=stream)
+        assert w12.verify(t, w, stream=stream) == (0, -1), f"{label}: encode does not verify"
+        e = t.num_escapes
+        base, esc_ptr = torch.empty_like(t.base), torch.empty_like(t.esc_ptr)
+        for _ in range(reps):
+            w12.encode_count(w, base, esc_ptr, stream=stream)
+        for _ in range(reps):
+            w12.encode_emit(w, t, stream=stream)
+        torch.cuda.synchronize()
+        assert w12.verify(t, w, stream=stream) == (0, -1), f"{label}: repeated emit does not verify"
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            w12.encode(w, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        res.append({"matrix": label, "n": n, "k": k, "reps": reps, "escapes": e,
+                    "encode_us": [round(a.elapsed_time(b) * 1e3, 1) for a, b in evs]})
+        del t, w, base, esc_ptr
+        torch.cuda.empty_cache()
+    print(json.dumps({"cases": res}))
+
+
+def encode_bytes(n, k, e):
+    """Algorithmic bytes of the three encode kernels: the count reads W and writes the bases and
+    escape counts; the scan reads and writes the counts; the emit reads W, the bases and pointers
+    and writes both planes (padding included) and the escapes."""
+    hib, lob = w12.layout_bytes(n, k)
+    return {"count": 2 * n * k + n + 4 * n, "scan": 8 * n + 4,
+            "emit": 2 * n * k + n + 4 * (n + 1) + hib + lob + 4 * e}
+
+
+def summarize_encode_trace(trace_csv, probe_json, command):
+    """rocprofv3 kernel durations of the --encode-probe runs: per matrix the medians of the count,
+    scan and emit kernels launched back to back (steady state), the encode's algorithmic bytes
+    over the sum of the medians against 8 TB/s, and the whole encode with its read-back of E
+    (event time, median)."""
+    import csv
+    with open(trace_csv) as f:
+        trace = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+    names = ("k_encode_count", "k_scan_counts", "k_encode_emit")
+    enc = [r for r in trace if any(kn in r["Kernel_Name"] for kn in names)]
+    with open(probe_json) as f:
+        probe = json.loads([ln for ln in f.read().splitlines() if ln.startswith("{")][-1])
+    dur = lambda rs: float(np.median([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]))
+    lines = ["# W12 encode kernel times (count, scan, emit) on the layer's matrices and the heavy-tail ones, "
+             "MI355X", "", "Command (run from the repository root):", "", "```", command, "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
+             "Kernel trace durations (`k_encode_count`, `k_scan_counts`, `k_encode_emit`), medians over R launches "
+             "of each kernel back to back (after one checked encode). Bytes are algorithmic: the count reads W "
+             "(2NK) and writes 5 B per channel; the scan reads and writes the counts; the emit reads W, bases and "
+             "pointers and writes the padded planes and 4 B per escape. The last three columns are the whole encode "
+             "as the library runs it at load time (count, scan, read-back of E, emit): the same kernels' durations "
+             "inside that sequence (count / scan / emit, medians of R), their sum against 8 TB/s, and the whole "
+             "encode's event time (median of R), read-back and host work included.", "",
+             "| matrix | N x K | escapes | count us | scan us | emit us | kernels us | count GB/s | emit GB/s | "
+             "encode GB/s | of 8 TB/s | in sequence us | of 8 TB/s | whole encode us |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    i = 0
+    for c in probe["cases"]:
+        r = c["reps"]
+        per = 3 + 2 * r + r + 3 * r
+        rows = enc[i:i + per]
+        i += per
+        assert len(rows) == per, "trace ends early"
+        counts, emits = rows[3:3 + 2 * r], rows[3 + 2 * r:3 + 3 * r]
+        assert all(names[j % 2] in x["Kernel_Name"] for j, x in enumerate(counts)), f"unexpected order at {c}"
+        assert all(names[2] in x["Kernel_Name"] for x in emits), f"unexpected order at {c}"
+        seq = rows[3 + 3 * r:]
+        assert all(names[j % 3] in x["Kernel_Name"] for j, x in enumerate(seq)), f"unexpected order at {c}"
+        med = {"count": dur(counts[0::2]), "scan": dur(counts[1::2]), "emit": dur(emits)}
+        in_seq = [dur(seq[j::3]) for j in range(3)]
+        by = encode_bytes(c["n"], c["k"], c["escapes"])
+        tot_us = sum(med.values())
+        tot_b = sum(by.values())
+        lines.append(f"| {c['matrix']} | {c['n']} x {c['k']} | {c['escapes']} | "
+                     f"{med['count']:.1f} | {med['scan']:.1f} | {med['emit']:.1f} | {tot_us:.1f} | "
+                     f"{by['count'] / med['count'] / 1e3:.0f} | {by['emit'] / med['emit'] / 1e3:.0f} | "
+                     f"{tot_b / tot_us / 1e3:.0f} | {tot_b / tot_us / 1e3 / HBM_PEAK_GBPS:.3f} | "
+                     f"{in_seq[0]:.1f} / {in_seq[1]:.1f} / {in_seq[2]:.1f} = {sum(in_seq):.1f} | "
+                     f"{tot_b / sum(in_seq) / 1e3 / HBM_PEAK_GBPS:.3f} | {float(np.median(c['encode_us'])):.1f} |")
+    assert i == len(enc), f"{len(enc) - i} encode kernels in the trace are not in the probe"
+    path = os.path.join(ROOT, "profiles", "encode_layer_kernel_trace.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 TIMELINE_CASES = (("gate_up", 16), ("down", 16), ("gate_up", 1), ("o_proj", 16))
@@ -1048,7 +1172,7 @@ def summarize_encode_lds(pmc_csv, fetch_csv):
     def by_kernel(path):
         agg = {}
         for r in _counter_rows(path):
-            for kn in ("k_encode_count", "k_encode_emit_blocks", "k_encode_emit_rows"):
+            for kn in ("k_encode_count", "k_encode_emit"):
                 if kn in r["Kernel_Name"]:
                     d = agg.setdefault(kn, {})
                     d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])

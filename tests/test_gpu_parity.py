@@ -24,8 +24,45 @@ def _exhaustive(shuffle):
     return w[None, :]
 
 
+def _fields(seed, n, k, lo, hi, zero_frac=0.0, special_frac=0.0):
+    """BF16 bit patterns with exponent fields drawn uniformly from lo..hi, random sign and
+    mantissa; a fraction set to +-0 and a fraction to inf/NaN (field 255)."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(lo, hi + 1, size=(n, k)).astype(np.uint16)
+    w = (rng.integers(0, 2, size=(n, k)).astype(np.uint16) << 15) | (e << 7) | rng.integers(0, 128, size=(n, k)).astype(np.uint16)
+    u = rng.random((n, k))
+    w[u < zero_frac] &= 0x8000
+    w[(u >= zero_frac) & (u < zero_frac + special_frac)] |= 0x7F80
+    return w
+
+
+def _bimodal(seed, n, k, gap):
+    """Half the weights of each row around field 100, half around field 100 + gap."""
+    w = _fields(seed, n, k, 98, 102)
+    hi = _fields(seed + 1, n, k, 98 + gap, 102 + gap)
+    pick = np.random.default_rng(seed + 2).random((n, k)) < 0.5
+    return np.where(pick, hi, w).astype(np.uint16)
+
+
+def _outliers_first(seed, n, k):
+    """Gaussian rows whose first 512 weights are 80 binades above the rest."""
+    w = S.layer_matrix(torch.Generator().manual_seed(seed), n, k)
+    w[:, :512] = _fields(seed, n, 512, 200, 205)
+    return w
+
+
 CASES = {
     "tiny_256x512": lambda: S.tiny_weights(0),
+    # exponent counts: bulk at the top or bottom of the field range, zeros, inf/NaN, two modes
+    # further apart than a window, outliers where each channel is first read, short rows
+    "top_fields_48x4100": lambda: _fields(11, 48, 4100, 238, 254, special_frac=0.05),
+    "bottom_fields_48x4100": lambda: _fields(12, 48, 4100, 1, 20, zero_frac=0.2),
+    "half_zeros_32x5000": lambda: _fields(13, 32, 5000, 110, 125, zero_frac=0.5),
+    "bimodal_32x5120": lambda: _bimodal(14, 32, 5120, 25),
+    "bimodal_close_32x5120": lambda: _bimodal(15, 32, 5120, 13),
+    "outliers_first_16x4096": lambda: _outliers_first(16, 16, 4096),
+    "short_9x7": lambda: _fields(17, 9, 7, 100, 130, zero_frac=0.1),
+    "multi_batch_5x8197": lambda: _fields(18, 5, 8197, 90, 140, zero_frac=0.01, special_frac=0.01),
     "exhaustive_1x65536": lambda: _exhaustive(False),
     "exhaustive_shuffled_1x65536": lambda: _exhaustive(True),
     "wide_37x1000": lambda: S.random_bits_matrix(np.random.default_rng(1), 37, 1000, "wide"),
@@ -63,16 +100,6 @@ def test_encode_matches_oracle(name):
     t = w12.encode(dev_weights(w))
     assert_encode_equal(t, ref)
     assert t.bits_per_weight() == pytest.approx(O.bits_per_weight(ref.n, ref.k, ref.num_escapes), rel=1e-15)
-
-
-@pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("blocks", [0, 1])
-def test_encode_both_emit_kernels(monkeypatch, name, blocks):
-    """Record emission by one wave per row and by one work-group per 16-row block (chosen by the
-    number of row blocks; W12_EMIT_BLOCKS forces either) gives the oracle's encoding."""
-    monkeypatch.setenv("W12_EMIT_BLOCKS", str(blocks))
-    w, ref = case(name)
-    assert_encode_equal(w12.encode(dev_weights(w)), ref)
 
 
 @pytest.mark.parametrize("name", list(CASES))
