@@ -294,15 +294,17 @@ __device__ __forceinline__ void issue_w(const GemmArgs& g, __amdgpu_buffer_rsrc_
   const uint32_t c = sl.c0 + sl.stride * j;
   const uint32_t vh = (c * kRowsPerBlock + r) * kChunkK;
   // the row block's plane offset rides in the per-lane offset: a scalar soffset would need
-  // the compiler to prove it uniform, and it cannot once scalar registers run out
+  // the compiler to prove it uniform, and it cannot once scalar registers run out.  The record
+  // planes are read once per launch: non-temporal loads keep them from displacing X, the
+  // escape slices and the partials in L2 (5-8% faster on gate_up and down, same-box A/B).
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void*)&st->hi[wave][rb][0], 16, (int)(soff_h[rb] + vh), 0, 0, 0);
+    dma16_nt(rh, &st->hi[wave][rb][0], soff_h[rb] + vh);
   if constexpr (!kQ) {
     const uint32_t cd = sl.cd0 + sl.stride * j;
     const uint32_t vl = cd * kLoChunkBytes + (lane & 7) * 16;
-    dma16(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
-    if (RB > 2) dma16(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
+    dma16_nt(rl, &st->lo[wave][0], sl.lo_rb0 + vl);
+    if (RB > 2) dma16_nt(rl, &st->lo[wave][64], sl.lo_rb1 + vl);
   }
 }
 

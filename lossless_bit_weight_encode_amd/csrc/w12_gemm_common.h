@@ -29,9 +29,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
+constexpr int kCachePolicyNT = 2;   // the cache-policy operand's non-temporal bit (gfx950)
 // 16 bytes per lane from the buffer into LDS: lane i's bytes land at dst + 16 i.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, 0);
+}
+// The same with the non-temporal cache policy (data read once: streamed through L2 without
+// displacing what is reused).
+__device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, kCachePolicyNT);
 }
 
 __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
