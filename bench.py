@@ -94,7 +94,7 @@ def timed_blocks(fn, iters, stream, blocks=5):
 READ_SIZES = {"o_proj_39MB": 39_340_032, "down_134MB": 133_693_440, "gate_up_267MB": 267_386_880,
               "1GiB": 1 << 30}
 # the read-probe shape the default run reports (the fastest of the --read-probe sweep)
-READ_BEST = (8, 2)   # (loads in flight per lane, 256-thread work-groups per CU)
+READ_BEST = (8, 1)   # (loads in flight per lane, 256-thread work-groups per CU)
 
 
 def read_ceiling(dev, stream, variants, sizes=READ_SIZES, reps=20):

@@ -49,7 +49,8 @@ __device__ __forceinline__ void count_outside(uint32_t e, uint32_t lo, uint32_t*
 // kBandBelow fields below the median over the lanes of each lane's largest field, so it covers
 // the channel's bulk even when a few large outliers are present.  A field outside the band is
 // still counted exactly, only more slowly.  Each lane issues kCountBatch loads (8 KB per wave)
-// before counting them.  At the end the lanes' counters are summed into the histogram, and the
+// before counting them.  They keep the default cache policy: what they leave in the caches
+// serves the emit, which reads W next.  At the end the lanes' counters are summed into the histogram, and the
 // window counts of all bases come from one prefix sum over the 256 fields.
 __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
     const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, const uint8_t* __restrict__ forced,
