@@ -549,6 +549,14 @@ __device__ unsigned long long w12_timeline[kMaxGrid * 16];
   } while (0)
 #endif
 
+// The work-group's logical index.  Work-groups are handed to the 8 XCDs in turn, so physical
+// block b runs on XCD b % 8; logical indices are laid out per XCD (XCD x takes a contiguous run),
+// which puts the work-groups that split a tile on one L2.
+__device__ __forceinline__ int64_t logical_wg(int64_t b, int64_t G) {
+  const int64_t x = b % 8, q = G / 8, r = G % 8;
+  return x * q + (x < r ? x : r) + b / 8;
+}
+
 // Stream-K bookkeeping: work-group w owns units [ubeg(w), ubeg(w+1)).
 __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w * g.units / g.G; }
 
@@ -784,8 +792,9 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   (void)tl_seg;
   const int wave = wave_id();
   // units, G and P are launch-wide: the same in every member of a group
-  const int64_t u_first = ubeg(ga.g[0], blockIdx.x);
-  const int64_t u_end = ubeg(ga.g[0], (int64_t)blockIdx.x + 1);
+  const int64_t wg = logical_wg(blockIdx.x, gridDim.x);
+  const int64_t u_first = ubeg(ga.g[0], wg);
+  const int64_t u_end = ubeg(ga.g[0], wg + 1);
   if (u_first >= u_end) return;
   const int gi_first = gemm_of(ga, u_first);
   // the first segment's product (the segment loop re-binds g and the resources per segment)
@@ -1109,7 +1118,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     const bool full = (cur.u == cur.t0) && (cur.seg_end == cur.t0 + g.upt);
     const int m0 = cur.m0 * MROWS;
     // partial slot: the work-group's first or last segment
-    const int64_t slot_i = 2 * (int64_t)blockIdx.x + ((cur.u == u_first) ? 0 : 1);
+    const int64_t slot_i = 2 * wg + ((cur.u == u_first) ? 0 : 1);
     const uint32_t slot = (uint32_t)(slot_i * TILE_ELEMS);
     // buffer stores (out-of-range offsets are dropped).  red, the partial tiles and Y's rows
     // share the order e = m * 64 + row: consecutive threads touch consecutive channels.
