@@ -549,14 +549,6 @@ __device__ unsigned long long w12_timeline[kMaxGrid * 16];
   } while (0)
 #endif
 
-// The work-group's logical index.  Work-groups are handed to the 8 XCDs in turn, so physical
-// block b runs on XCD b % 8; logical indices are laid out per XCD (XCD x takes a contiguous run),
-// which puts the work-groups that split a tile on one L2.
-__device__ __forceinline__ int64_t logical_wg(int64_t b, int64_t G) {
-  const int64_t x = b % 8, q = G / 8, r = G % 8;
-  return x * q + (x < r ? x : r) + b / 8;
-}
-
 // Stream-K bookkeeping: work-group w owns units [ubeg(w), ubeg(w+1)).
 __device__ __forceinline__ int64_t ubeg(const GemmArgs& g, int64_t w) { return w * g.units / g.G; }
 

@@ -43,6 +43,14 @@ __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, void* dst, ui
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)voff, 0, 0, kCachePolicyNT);
 }
 
+// The work-group's logical index.  Work-groups are handed to the 8 XCDs in turn, so physical
+// block b runs on XCD b % 8; logical indices are laid out per XCD (XCD x takes a contiguous run),
+// which puts the work-groups that split a tile (or share its weights) on one L2.
+__device__ __forceinline__ int64_t logical_wg(int64_t b, int64_t G) {
+  const int64_t x = b % 8, q = G / 8, r = G % 8;
+  return x * q + (x < r ? x : r) + b / 8;
+}
+
 __device__ __forceinline__ uint32_t lds_off(const void* p) { return (uint32_t)(uintptr_t)(lds_u8*)p; }
 
 // Wait until at most N vector-memory instructions of this wave are outstanding.

@@ -140,14 +140,20 @@ __device__ __forceinline__ void wdma_setup(const WideArgs& g, const WSeg& s, int
 template <int TM, bool kQ>
 __device__ __forceinline__ void wide_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rh,
                                            __amdgpu_buffer_rsrc_t rl, const WDma& d, uint32_t j, uint32_t nch,
-                                           WideStage<TM>* st, int wave) {
+                                           WideStage<TM>* st, int wave, bool once) {
 #pragma unroll
   for (int i = 0; i < WideCfg<TM>::kXDma; ++i) {
     const bool ok = d.x[i] != kOutOfRange && 2 * j + d.xkk[i] < nch;
     dma16(rx, &st->x[wave * WideCfg<TM>::kXDma + i][0], ok ? d.x[i] + 64u * j : kOutOfRange);
   }
-  dma16(rh, &st->hi[2 * wave][0][0], d.h != kOutOfRange ? d.h + 512u * j : kOutOfRange);
-  if (!kQ && wave < 4) dma16(rl, &st->lo[4 * wave][0][0], d.l != kOutOfRange ? d.l + 256u * j : kOutOfRange);
+  const uint32_t oh = d.h != kOutOfRange ? d.h + 512u * j : kOutOfRange;
+  if (once) dma16_nt(rh, &st->hi[2 * wave][0][0], oh);
+  else dma16(rh, &st->hi[2 * wave][0][0], oh);
+  if (!kQ && wave < 4) {
+    const uint32_t ol = d.l != kOutOfRange ? d.l + 256u * j : kOutOfRange;
+    if (once) dma16_nt(rl, &st->lo[4 * wave][0][0], ol);
+    else dma16(rl, &st->lo[4 * wave][0][0], ol);
+  }
 }
 
 // Wait until stage j has landed for this wave: at most n newer stages (V DMAs each) remain.
@@ -274,6 +280,9 @@ void k_gemm_wide(WideArgs g) {
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(g.Y, g.y_bytes);
   const __amdgpu_buffer_rsrc_t rpart = make_rsrc(g.P, g.p_bytes);
 
+  // records read by one tile only (a single m tile) use the non-temporal cache policy: 2-3%
+  // faster at M <= 256; with two m tiles the second reads the same records from the caches
+  const bool once = g.MT == 1;
   const int64_t u_first = wubeg(g, blockIdx.x);
   const int64_t u_end = wubeg(g, (int64_t)blockIdx.x + 1);
   if (u_first >= u_end) return;
@@ -318,7 +327,7 @@ void k_gemm_wide(WideArgs g) {
     WDma dm;
     wdma_setup<TM>(g, s, wave, lane, dm);
     const uint32_t nch = s.cs1 - s.cs0;
-    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave);
+    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave, once);
     wait_vm_all();
     barrier();
     WEsc cur[2];
@@ -343,7 +352,7 @@ void k_gemm_wide(WideArgs g) {
       barrier();   // stage j visible to all waves; every wave is done with stage j - 1
       if (j + NS - 1 < s.nst) {
         const uint32_t ws = slot == 0 ? NS - 1 : slot - 1;
-        wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave);
+        wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave, once);
       }
       // one test per stage: does any lane of the wave hold an escape before the stage's end?
       const uint32_t kend = (s.cs0 + 2 * j + 2) * kChunkK;
