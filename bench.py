@@ -1243,8 +1243,9 @@ def checkpoint_leg(enc, w_dev, names, reps=3):
 
 def full_model_leg(dev, stream, n_layers, m, reps=5):
     """The full-model weight stream: n_layers decoder layers (each drawn from its own seed on
-    the GPU's generator, see w12_synth.layer_device), encoded and checked bit for bit at load
-    time, then all 4 n_layers GEMMs launched back to back at M=m.  Before every timed pass a
+    the GPU's generator, see w12_synth.layer_device), encoded (one read-back of the escape counts
+    per layer, w12.encode_many) and checked bit for bit at load time, then all 4 n_layers GEMMs
+    launched back to back at M=m.  Before every timed pass a
     1 GiB buffer is written, so the pass starts from cold weights (the W12 model is far larger
     than the 256 MB Infinity Cache in any case)."""
     names = list(S.LAYER_ORDER)
@@ -1256,7 +1257,7 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
         torch.cuda.synchronize()
         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         e0.record(stream)
-        enc = {nm: w12.encode(lay[nm], stream=stream) for nm in names}
+        enc = dict(zip(names, w12.encode_many([lay[nm] for nm in names], stream=stream)))
         e1.record(stream)
         for i, nm in enumerate(names):
             w12.verify_async(enc[nm], lay[nm], res[li, i], stream=stream)

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     encode,
     encode_count,
     encode_emit,
+    encode_many,
     file_index,
     GROUP_MAX,
     gemm,

@@ -222,6 +222,31 @@ def encode(w: torch.Tensor, forced_base: torch.Tensor | None = None, stream=None
     return t
 
 
+def encode_many(ws: list, stream=None) -> list:
+    """encode() of several BF16 matrices with a single read-back: every count pass is launched,
+    the escape counts E of all of them come back in one copy (one synchronisation), then every
+    emit is launched.  Returns the W12Tensors in the order of ws."""
+    with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream()):
+        parts = []
+        for w in ws:
+            _require_cuda(w)
+            _bits16(w)
+            n, k = w.shape
+            base, hi, lo, esc_ptr = alloc_planes(n, k, w.device)
+            encode_count(w, base, esc_ptr)
+            parts.append((w, n, k, base, hi, lo, esc_ptr))
+        if not parts:
+            return []
+        es = torch.stack([p[6][p[1]] for p in parts]).cpu().tolist()   # copies and waits on the same stream
+        out = []
+        for (w, n, k, base, hi, lo, esc_ptr), e in zip(parts, es):
+            esc = torch.empty(int(e) & 0xFFFFFFFF, dtype=torch.int32, device=w.device)
+            t = W12Tensor(n, k, base, hi, lo, esc_ptr, esc)
+            encode_emit(w, t)
+            out.append(t)
+    return out
+
+
 def decode(t: W12Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     if out is None:
         # rows padded to a multiple of 8 elements (the 16-byte store granule), viewed to K

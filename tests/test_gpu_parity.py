@@ -472,3 +472,26 @@ def test_side_stream_encode_verify_gemm():
     for name in ("base", "hi", "lo", "esc_ptr", "esc"):
         assert torch.equal(getattr(t, name), getattr(t_ref, name)), name
     torch.cuda.synchronize()
+
+
+def test_encode_many_matches_encode():
+    """encode_many (one read-back of the escape counts for several matrices) gives, tensor for
+    tensor, exactly what encode gives for each alone, also on a side stream, and an empty list
+    gives an empty list."""
+    names = ["gauss_300x4096", "ragged_17x33", "all_escapes_20x96", "no_escapes_64x512", "heavy_64x2048"]
+    ws = [dev_weights(case(nm)[0]) for nm in names]
+    refs = [w12.encode(w) for w in ws]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for stream in (None, s):
+        got = w12.encode_many(ws, stream=stream)
+        if stream is not None:
+            stream.synchronize()
+        assert len(got) == len(refs)
+        for nm, t, r in zip(names, got, refs):
+            assert (t.n, t.k, t.num_escapes) == (r.n, r.k, r.num_escapes), nm
+            for field in ("base", "hi", "lo", "esc_ptr", "esc"):
+                assert torch.equal(getattr(t, field), getattr(r, field)), (nm, field)
+        for nm, t in zip(names, got):
+            assert_encode_equal(t, case(nm)[1])
+    assert w12.encode_many([]) == []
