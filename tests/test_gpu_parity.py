@@ -74,6 +74,11 @@ CASES = {
     "all_escapes_20x96": lambda: np.zeros((20, 96), dtype=np.uint16),
     # more channels than one pass of the escape-count scan keeps in registers
     "tall_100003x16": lambda: S.random_bits_matrix(np.random.default_rng(6), 100003, 16, "wide"),
+    # channel counts at the escape-count scan's chunk boundaries (32768 counts per chunk)
+    "scan_edge_32767x24": lambda: S.random_bits_matrix(np.random.default_rng(21), 32767, 24, "wide"),
+    "scan_edge_32768x24": lambda: S.random_bits_matrix(np.random.default_rng(22), 32768, 24, "wide"),
+    "scan_edge_32769x24": lambda: S.random_bits_matrix(np.random.default_rng(23), 32769, 24, "wide"),
+    "scan_edge_65537x8": lambda: S.random_bits_matrix(np.random.default_rng(24), 65537, 8, "wide"),
     # every weight in [1, 2): one binade, no escape at all (E = 0, no escape array)
     "no_escapes_64x512": lambda: S.to_bf16_bits(1.0 + torch.rand(64, 512, generator=torch.Generator().manual_seed(8))),
 }
