@@ -367,7 +367,11 @@ def test_gemm_bitwise_deterministic(m):
 
 @pytest.mark.parametrize("name,m,grid", [("gauss_300x4096", 1, 4), ("gauss_300x4096", 16, 3),
                                          ("heavy_64x2048", 100, 1), ("wide_37x1000", 100, 1),
-                                         ("tiny_256x512", 64, 3), ("ragged_17x33", 70, 1)])
+                                         ("tiny_256x512", 64, 3), ("ragged_17x33", 70, 1),
+                                         # grids that are not a multiple of the 8 XCDs: the logical
+                                         # work-group order has full rounds and a remainder
+                                         ("gauss_300x4096", 16, 13), ("gauss_300x4096", 2, 37),
+                                         ("heavy_64x2048", 32, 7)])
 def test_gemm_small_grid(monkeypatch, name, m, grid):
     """More tiles than work-groups (the grid capped with W12_MAX_GRID): work-group ranges span
     several tiles, with partial first and last segments and whole tiles between them.  Y is
