@@ -50,8 +50,8 @@ __device__ __forceinline__ void count_outside(uint32_t e, uint32_t lo, uint32_t*
 // the channel's bulk even when a few large outliers are present.  A field outside the band is
 // still counted exactly, only more slowly.  Each lane issues kCountBatch loads (8 KB per wave)
 // before counting them.  They keep the default cache policy: what they leave in the caches
-// serves the emit, which reads W next.  At the end the lanes' counters are summed into the histogram, and the
-// window counts of all bases come from one prefix sum over the 256 fields.
+// serves the emit, which reads W next.  At the end the lanes' counters are summed into the
+// histogram, and the window counts of all bases come from one prefix sum over the 256 fields.
 __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
     const uint16_t* __restrict__ W, int32_t N, int32_t K, int64_t ldw, const uint8_t* __restrict__ forced,
     uint8_t* __restrict__ base, uint32_t* __restrict__ esc_ptr) {
@@ -184,11 +184,12 @@ __global__ __launch_bounds__(kCountWaves * kWave) void k_encode_count(
 }
 
 // esc_ptr[0] = 0 and an inclusive scan of the counts in esc_ptr[1..N] (one work-group).
-// The counts stream through LDS in chunks of kScanChunk: coalesced loads into LDS; each thread
-// sums and then scans its kScanPer contiguous counts there (one pad word every 32 keeps those
-// strided reads to 2-way bank conflicts); wave shuffles and one pass over the wave totals give
-// each thread its offset; coalesced stores write the chunk back, and the chunk's total carries
-// into the next one.
+// The counts stream through LDS in chunks of kScanChunk: coalesced loads into LDS (all of a
+// chunk's loads in flight at once); each thread sums and then scans its kScanPer contiguous
+// counts there (with one pad word every 32 slots, consecutive threads' runs start 33 words
+// apart, so their reads fall in distinct banks); wave shuffles and one pass over the wave
+// totals give each thread its offset; coalesced stores write the chunk back, and the chunk's
+// total carries into the next one.
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 32;
 constexpr int kScanChunk = kScanThreads * kScanPer;

@@ -3,8 +3,9 @@
 // What the GEMM must do is set by the SpecPilot summary page, method bullet of section 4.1:
 // decode W12 records in registers inside a stream-K GEMM, and reduce the K split in an order
 // fixed in advance, so repeated runs give identical bits.  This gfx950 version:
-//   * streams the hi/lo record planes from HBM into a per-wave two-stage LDS ring with
-//     buffer-to-LDS DMA loads (no registers held while a stage is in flight), reads each
+//   * streams the hi/lo record planes from HBM into a per-wave LDS ring (two stages; three for
+//     the 64-row tiles) with non-temporal buffer-to-LDS DMA loads (no registers held while a
+//     stage is in flight; the planes are read once and stream through L2), reads each
 //     lane's 16 + 8 bytes back, decodes them to BF16 pairs in registers (decode16) and
 //     patches the escapes of the lane's chunk from its channel's escape list, which sits in
 //     LDS (copied one segment ahead);
@@ -12,11 +13,12 @@
 //     fixed butterfly over the 4 lane groups and a fixed wave order through LDS; X rides the
 //     ring;
 //   * larger M: the decoded chunk is the B operand of v_mfma_f32_16x16x32_bf16 (16 rows of W x
-//     32 k) and X rows (padded to 16) are the A operand, double-buffered in registers;
+//     32 k) and X rows (padded to 16) are the A operand, staged in the LDS ring beside the
+//     records (16, 48 and 64 rows) or double-buffered in registers (32 rows);
 //   * schedules work stream-K style: the grid is at most the number of work-groups resident at
-//     once, and work-group w takes the contiguous range [w U / G, (w+1) U / G) of the U = tiles
-//     x units work units (a unit is 16 chunks of one tile), so every work-group streams the
-//     same number of bytes.  A tile covered by several work-groups gets one partial per
+//     once, and work-group w (its logical index, laid out per XCD) takes the contiguous range
+//     [w U / G, (w+1) U / G) of the U = tiles x units work units (a unit is 16 chunks of one
+//     tile), so every work-group streams the same number of bytes.  A tile covered by several work-groups gets one partial per
 //     segment; the last segment to finish sums them in segment order (a fixed order set by
 //     (M, N, K, G)), with no floating-point atomics.
 //

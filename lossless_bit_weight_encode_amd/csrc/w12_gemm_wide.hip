@@ -11,7 +11,8 @@
 //     accumulators of v_mfma_f32_32x32x16_bf16 with X as the A operand and the decoded
 //     weights as the B operand;
 //   * a stage is 32 k: the X rows of the tile, already in MFMA fragment order, and the hi/lo
-//     records of the 256 channels arrive by buffer-to-LDS DMA in a ring of NS stages;
+//     records of the 256 channels arrive by buffer-to-LDS DMA in a ring of NS stages (the
+//     records with the non-temporal cache policy when no other m tile reads them);
 //   * each lane reads its X fragments and 8 records of each of its 2 channels from LDS,
 //     decodes the records straight into the B operand and patches escapes from the segment's
 //     escape slice in LDS (walked in global memory when the slice does not fit);
