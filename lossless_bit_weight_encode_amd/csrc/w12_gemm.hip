@@ -1331,8 +1331,12 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
   const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
   p.counter_bytes = kCounterBytes;
   p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
-  // ragged K: room for X padded to whole chunks
-  p.xpad_bytes = (K % kChunkK) ? ((uint64_t)M * (uint64_t)Kc * kChunkK * 2 + 255) / 256 * 256 : 0;
+  // the wide tiles: room for X in operand order (every m tile whole, zeros past M and K);
+  // the other paths, ragged K: room for X padded to whole chunks
+  if (p.path == 3)
+    p.xpad_bytes = ((uint64_t)p.m_tiles * p.m_tile * (uint64_t)Kc * kChunkK * 2 + 255) / 256 * 256;
+  else
+    p.xpad_bytes = (K % kChunkK) ? ((uint64_t)M * (uint64_t)Kc * kChunkK * 2 + 255) / 256 * 256 : 0;
   p.ws_bytes = p.counter_bytes + p.partial_bytes + p.xpad_bytes;
   return p;
 }
@@ -1384,6 +1388,8 @@ static void fill_args(GemmArgs& a, const GemmPlan& p, const uint16_t* X, int32_t
 
 hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t ldx, const w12_tensor* t, float* Y,
                        int64_t ldy, void* ws, bool qpass, hipStream_t stream) {
+  // the wide tiles rearrange X themselves (padding included)
+  if (p.path == 3) return launch_gemm_wide(p, X, M, ldx, t, Y, ldy, ws, qpass, stream);
   GemmArgs a;
   a.Kc = num_chunks(t->K);
   if (p.xpad_bytes) {
@@ -1395,7 +1401,6 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
     X = xp;
     ldx = kp;
   }
-  if (p.path == 3) return launch_gemm_wide(p, X, M, ldx, t, Y, ldy, ws, qpass, stream);
   fill_args(a, p, X, M, ldx, t, Y, ldy, ws);
   a.ubase = 0;
   a.tiles = p.tiles;

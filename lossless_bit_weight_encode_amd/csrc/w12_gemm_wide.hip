@@ -10,9 +10,11 @@
 //     wave (wm, wn) owns rows 32 TM wm .. +32 TM and channels 64 wn .. +64, as TM x 2
 //     accumulators of v_mfma_f32_32x32x16_bf16 with X as the A operand and the decoded
 //     weights as the B operand;
-//   * a stage is 32 k: the X rows of the tile, already in MFMA fragment order, and the hi/lo
-//     records of the 256 channels arrive by buffer-to-LDS DMA in a ring of NS stages (the
-//     records with the non-temporal cache policy when no other m tile reads them);
+//   * X is rearranged once per call (k_pack_x_wide) into MFMA operand order in the
+//     workspace: 1 KB per 32 rows and 16 k, so that each X DMA is one contiguous 1 KB read
+//     (read in place, every DMA would gather 32 separate 32-byte pieces of rows);
+//   * a stage is 32 k: the X fragments of the tile and the hi/lo records of the 256 channels
+//     arrive by buffer-to-LDS DMA in a ring of NS stages;
 //   * each lane reads its X fragments and 8 records of each of its 2 channels from LDS,
 //     decodes the records straight into the B operand and patches escapes from the segment's
 //     escape slice in LDS (walked in global memory when the slice does not fit);
@@ -46,8 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4w __attribute__((ext_vector_type(4)));
 
 struct WideArgs {
-  const uint16_t* X;
-  int64_t ldx;
+  const uint4* X;       // X in operand order (k_pack_x_wide)
   const uint8_t* base;
   const uint8_t* hi;
   const uint8_t* lo;
@@ -79,7 +80,7 @@ struct WideStage {
 template <int TM>
 struct WideCfg {
   static constexpr int kRows = 64 * TM;                 // rows of X per tile
-  static constexpr int kNS = TM == 4 ? 4 : 6;           // ring stages (about 120 KB of LDS)
+  static constexpr int kNS = TM == 4 ? 5 : 6;           // ring stages (140 / 120 KB of LDS)
   static constexpr int kXDma = TM / 2;                  // X fragments each wave fetches per stage
   static constexpr int kTile = kRows * kWCols;          // elements of a tile
   static constexpr int kF4 = 8 * TM;                    // float4 groups of accumulators per lane
@@ -90,6 +91,7 @@ __device__ __forceinline__ int64_t wubeg(const WideArgs& g, int64_t w) { return 
 // A segment: the stretch of one tile inside a work-group's unit range.
 struct WSeg {
   int64_t u, seg_end, tile, t0, rg, n0;
+  int mt;             // m tile
   int mrow0;          // first row of X
   uint32_t cs0, cs1;  // chunks [cs0, cs1) of the tile's K
   uint32_t nst;       // stages (2 chunks each; the last may hold one)
@@ -102,7 +104,8 @@ __device__ __forceinline__ void wseg(const WideArgs& g, int64_t u, int64_t u_end
   s.t0 = s.tile * g.upt;
   s.seg_end = u_end < s.t0 + g.upt ? u_end : s.t0 + g.upt;
   s.rg = s.tile / g.MT;
-  s.mrow0 = (int)(s.tile - s.rg * g.MT) * WideCfg<TM>::kRows;
+  s.mt = (int)(s.tile - s.rg * g.MT);
+  s.mrow0 = s.mt * WideCfg<TM>::kRows;
   s.n0 = s.rg * kWCols;
   s.cs0 = (uint32_t)((u - s.t0) * kWUnitChunks);
   const int64_t c1 = (s.seg_end - s.t0) * kWUnitChunks;
@@ -110,8 +113,9 @@ __device__ __forceinline__ void wseg(const WideArgs& g, int64_t u, int64_t u_end
   s.nst = (s.cs1 - s.cs0 + 1) / 2;
 }
 
-// Per-lane DMA byte offsets of a segment's stage 0 (stage j adds j times 64, 512 and 256
-// bytes: two chunks of X, hi and lo); kOutOfRange for rows past M or row blocks past N.
+// Per-lane DMA byte offsets of a segment's stage 0 (stage j adds j times 4096 TM, 512 and
+// 256 bytes: two chunks of X, hi and lo); kOutOfRange for row blocks past N (the rows of X
+// past M are zeros in the rearranged copy).
 struct WDma {
   uint32_t x[2];     // this wave's X fragments (at most 2 per stage)
   uint32_t xkk[2];   // their chunk within the stage
@@ -124,9 +128,7 @@ __device__ __forceinline__ void wdma_setup(const WideArgs& g, const WSeg& s, int
   for (int i = 0; i < WideCfg<TM>::kXDma; ++i) {
     const int f = wave * WideCfg<TM>::kXDma + i;
     const int kk = f / (2 * TM), mb = f % (2 * TM);
-    const int m = s.mrow0 + 32 * mb + (lane & 31);
-    d.x[i] = m < g.M ? (uint32_t)(((int64_t)m * g.ldx + (int64_t)(s.cs0 + kk) * kChunkK + 8 * (lane >> 5)) * 2)
-                     : kOutOfRange;
+    d.x[i] = (uint32_t)((((int64_t)s.mt * g.Kc + s.cs0 + kk) * (2 * TM) + mb) * 1024 + 16 * lane);
     d.xkk[i] = (uint32_t)kk;
   }
   const int64_t rbh = s.rg * kWRB + 2 * wave + (lane >> 5);
@@ -141,20 +143,14 @@ __device__ __forceinline__ void wdma_setup(const WideArgs& g, const WSeg& s, int
 template <int TM, bool kQ>
 __device__ __forceinline__ void wide_issue(__amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rh,
                                            __amdgpu_buffer_rsrc_t rl, const WDma& d, uint32_t j, uint32_t nch,
-                                           WideStage<TM>* st, int wave, bool once) {
+                                           WideStage<TM>* st, int wave) {
 #pragma unroll
   for (int i = 0; i < WideCfg<TM>::kXDma; ++i) {
     const bool ok = d.x[i] != kOutOfRange && 2 * j + d.xkk[i] < nch;
-    dma16(rx, &st->x[wave * WideCfg<TM>::kXDma + i][0], ok ? d.x[i] + 64u * j : kOutOfRange);
+    dma16(rx, &st->x[wave * WideCfg<TM>::kXDma + i][0], ok ? d.x[i] + (uint32_t)(4096 * TM) * j : kOutOfRange);
   }
-  const uint32_t oh = d.h != kOutOfRange ? d.h + 512u * j : kOutOfRange;
-  if (once) dma16_nt(rh, &st->hi[2 * wave][0][0], oh);
-  else dma16(rh, &st->hi[2 * wave][0][0], oh);
-  if (!kQ && wave < 4) {
-    const uint32_t ol = d.l != kOutOfRange ? d.l + 256u * j : kOutOfRange;
-    if (once) dma16_nt(rl, &st->lo[4 * wave][0][0], ol);
-    else dma16(rl, &st->lo[4 * wave][0][0], ol);
-  }
+  dma16(rh, &st->hi[2 * wave][0][0], d.h != kOutOfRange ? d.h + 512u * j : kOutOfRange);
+  if (!kQ && wave < 4) dma16(rl, &st->lo[4 * wave][0][0], d.l != kOutOfRange ? d.l + 256u * j : kOutOfRange);
 }
 
 // Wait until stage j has landed for this wave: at most n newer stages (V DMAs each) remain.
@@ -281,9 +277,6 @@ void k_gemm_wide(WideArgs g) {
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(g.Y, g.y_bytes);
   const __amdgpu_buffer_rsrc_t rpart = make_rsrc(g.P, g.p_bytes);
 
-  // records read by one tile only (a single m tile) use the non-temporal cache policy: 2-3%
-  // faster at M <= 256; with two m tiles the second reads the same records from the caches
-  const bool once = g.MT == 1;
   const int64_t u_first = wubeg(g, blockIdx.x);
   const int64_t u_end = wubeg(g, (int64_t)blockIdx.x + 1);
   if (u_first >= u_end) return;
@@ -328,7 +321,7 @@ void k_gemm_wide(WideArgs g) {
     WDma dm;
     wdma_setup<TM>(g, s, wave, lane, dm);
     const uint32_t nch = s.cs1 - s.cs0;
-    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave, once);
+    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave);
     wait_vm_all();
     barrier();
     WEsc cur[2];
@@ -353,7 +346,7 @@ void k_gemm_wide(WideArgs g) {
       barrier();   // stage j visible to all waves; every wave is done with stage j - 1
       if (j + NS - 1 < s.nst) {
         const uint32_t ws = slot == 0 ? NS - 1 : slot - 1;
-        wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave, once);
+        wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave);
       }
       // one test per stage: does any lane of the wave hold an escape before the stage's end?
       const uint32_t kend = (s.cs0 + 2 * j + 2) * kChunkK;
@@ -475,6 +468,42 @@ void k_gemm_wide(WideArgs g) {
   }
 }
 
+// X rearranged for the wide tiles.  Fragment (t, c, b), 1 KB at ((t Kc + c) 2TM + b) KB,
+// holds for lane l the 8 elements of row 64 TM t + 32 b + l % 32 at k = 16 c + 8 (l / 32)
+// .. + 7, zeros past M and K: what lane l of the A operand of v_mfma_f32_32x32x16_bf16 takes
+// for rows 32 b .. + 31 and k 16 c .. + 15 of m tile t.  One thread per 8 elements of a row,
+// in row order (coalesced reads, 16-byte writes).
+template <int TM>
+__global__ __launch_bounds__(256) void k_pack_x_wide(const uint16_t* __restrict__ X, int64_t ldx, int32_t M,
+                                                     int32_t K, int32_t Kc, int64_t rows, uint4* __restrict__ out) {
+  const int64_t groups = 2 * (int64_t)Kc;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * groups) return;
+  const int64_t m = i / groups;
+  const int g = (int)(i - m * groups);
+  const int64_t k0 = 8 * (int64_t)g;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (m < M) {
+    const uint16_t* p = X + m * ldx + k0;
+    if (k0 + 8 <= K && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+      v = *reinterpret_cast<const uint4*>(p);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t a = k0 + 2 * j < K ? p[2 * j] : 0u;
+        const uint32_t b = k0 + 2 * j + 1 < K ? p[2 * j + 1] : 0u;
+        w[j] = a | (b << 16);
+      }
+      v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  const int64_t t = m / WideCfg<TM>::kRows;
+  const int r = (int)(m - t * WideCfg<TM>::kRows);
+  const int lane = (r & 31) + 32 * (g & 1);
+  out[((t * Kc + (g >> 1)) * (2 * TM) + (r >> 5)) * kWave + lane] = v;
+}
+
 template <int TM, bool kQ = false>
 static int occupancy_wide(int fallback) {
   static std::once_flag once;
@@ -499,8 +528,14 @@ hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int
                             float* Y, int64_t ldy, void* ws, bool qpass, hipStream_t stream) {
   WideArgs a;
   a.Kc = (int32_t)num_chunks(t->K);
-  a.X = X;
-  a.ldx = ldx;
+  // X into operand order, in the workspace after the partials
+  uint4* xp = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes + p.partial_bytes);
+  const int64_t rows = (int64_t)p.m_tiles * p.m_tile;
+  const int64_t threads = rows * 2 * a.Kc;
+  const dim3 pgrid((unsigned)((threads + 255) / 256)), pblock(256);
+  if (p.m_tile <= 128) hipLaunchKernelGGL((k_pack_x_wide<2>), pgrid, pblock, 0, stream, X, ldx, M, t->K, a.Kc, rows, xp);
+  else hipLaunchKernelGGL((k_pack_x_wide<4>), pgrid, pblock, 0, stream, X, ldx, M, t->K, a.Kc, rows, xp);
+  a.X = xp;
   a.base = t->base;
   a.hi = t->hi;
   a.lo = t->lo;
@@ -519,7 +554,7 @@ hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int
   const uint64_t chunks = (uint64_t)a.Nb * (uint64_t)a.Kc;
   a.hi_bytes = (uint32_t)(chunks * kHiChunkBytes);
   a.lo_bytes = (uint32_t)(chunks * kLoChunkBytes);
-  a.x_bytes = (uint32_t)(((uint64_t)(M - 1) * (uint64_t)ldx + (uint64_t)a.Kc * kChunkK) * 2u);
+  a.x_bytes = (uint32_t)((uint64_t)rows * (uint64_t)a.Kc * kChunkK * 2u);
   a.esc_bytes = (uint32_t)((uint64_t)t->num_escapes * 4u);
   a.Y = Y;
   a.ldy = ldy;

@@ -166,9 +166,14 @@ def test_gemm_plan_is_consistent(m, n, k):
     if tiles <= p["grid"]:
         # a whole multiple of the tiles when that keeps 3/4 of the grid: no range crosses a tile
         assert p["grid"] % tiles == 0 or p["grid"] * 3 > 4 * (p["grid"] // tiles) * tiles
-    # counters + two partial tiles (tile channels x m tile) per work-group (+ X padded to whole
-    # 16-k chunks when K is ragged)
-    xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
+    # counters + two partial tiles (tile channels x m tile) per work-group, + a copy of X: for
+    # the wide tiles every m tile whole in operand order, otherwise X padded to whole 16-k
+    # chunks when K is ragged
+    if p["path"] == 3:
+        mt = (m + p["m_tile"] - 1) // p["m_tile"]
+        xpad = (mt * p["m_tile"] * kc * 16 * 2 + 255) // 256 * 256
+    else:
+        xpad = 0 if k % 16 == 0 else (m * kc * 16 * 2 + 255) // 256 * 256
     assert p["workspace_bytes"] == p["counter_bytes"] + 2 * p["grid"] * 16 * rb * p["m_tile"] * 4 + xpad
     assert w12.gemm_workspace_size(m, n, k) == p["workspace_bytes"]
 
