@@ -130,7 +130,10 @@ int w12_unpack_records(const w12_tensor *t, uint16_t *rec, int64_t ldr, hipStrea
 
 /* Bytes of device workspace w12_gemm needs for M rows of X against W[N][K]. Host only.
  * The workspace starts with a 16 KB region of 32-bit arrival counters (split-K bookkeeping;
- * the same region for every plan, single or grouped) followed by the FP32 slice partials.
+ * the same region for every plan, single or grouped) followed by the FP32 slice partials
+ * and, where the plan needs it, a copy of X that the call writes itself: for M >= 65 X
+ * rearranged into the matrix cores' operand order, otherwise, for K % 16 != 0, X padded
+ * with zeros to whole 16-k chunks.
  * The size follows the plan, so a change of W12_GEMV_MAX_M between sizing and calling can
  * make the workspace too small (reported as W12_ERR_WORKSPACE_TOO_SMALL). */
 int w12_gemm_workspace_size(int32_t M, int32_t N, int32_t K, uint64_t *bytes);
