@@ -327,6 +327,7 @@ template <int M>
 struct GemvPath {
   static constexpr int kMRows = M;
   static constexpr int kWavesPerEU = 2;   // register budget: two work-groups per CU
+  static constexpr bool kDenseOk = M <= 4;   // the escape windows' registers fit (dense instantiation)
   static constexpr bool kXInLds = true;
   static constexpr int kWStages = 2;      // W ring stages
   static constexpr int kVmemPerStage = 7;   // 6 W DMA + 1 X DMA
@@ -412,6 +413,7 @@ template <int MB>
 struct MfmaPath {
   static constexpr int kMRows = MB * 16;
   static constexpr int kWavesPerEU = MB <= 2 ? 2 : 1;   // register budget: two work-groups per CU up to 32 rows
+  static constexpr bool kDenseOk = MB == 1;   // the escape windows' registers fit (dense instantiation)
   // X in LDS for 16 rows (two work-groups per CU fit) and for 48-64 rows (one per CU in any
   // case: 5-7% faster than register X); 32-row tiles keep X in registers, which keeps two
   // work-groups per CU (with X in LDS they would need 98 KB each)
@@ -650,6 +652,88 @@ __device__ __forceinline__ void esc_apply(LaneEsc& c, const uint32_t* __restrict
   }
 }
 
+// Escape-dense tensors (lists longer than the LDS slice on average) run an instantiation of
+// their own, in which every segment walks its lists in global memory with the contiguous
+// mapping.  Each lane keeps the next four entries of each of its lists in registers.  They
+// are loaded right after a step's escapes are patched, before the next stage's loads, so the
+// wait for them leaves that stage in flight (loads complete in issue order); a one-entry
+// walk that waits on the spot would drain every stage in flight at each entry.  An escaped
+// position holds record 0, the only record that decodes to the window base with a zero
+// mantissa, so a chunk holds at most as many escapes as such values: a lane reads no more
+// entries than that, and only a chunk with more than four reads past its window (one entry
+// at a time, waited for on the spot).
+struct EscWin {
+  uint4 v;        // entries [pos, pos + 4) of the lane's list (past E: zeros, never used)
+  uint32_t pos;
+};
+
+__device__ __forceinline__ void load_win(__amdgpu_buffer_rsrc_t re, const LaneEsc& c, EscWin& w) {
+  w.pos = c.pos;
+  const uint32_t off = c.pos < c.end ? c.pos * 4u : 0u;
+  w.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(re, (int)off, 0, 0));
+}
+
+// Decoded weights of a chunk equal to the window base with a zero mantissa (record 0).
+__device__ __forceinline__ uint32_t zero_records(const uint32_t d[8], uint32_t bb2) {
+  uint32_t z = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t x = d[p] ^ bb2;
+    z += (x & 0xFFFFu) == 0u ? 1u : 0u;
+    z += (x >> 16) == 0u ? 1u : 0u;
+  }
+  return z;
+}
+
+// Patch the escapes of chunk [k0, k0 + 16) from the window; z bounds the entries read.
+__device__ __forceinline__ void esc_apply_win(LaneEsc& c, const EscWin& w, const uint32_t* __restrict__ esc,
+                                              uint32_t k0, uint32_t d[8], uint32_t z) {
+  for (uint32_t i = 0; i < z; ++i) {
+    if (c.pos >= c.end) break;
+    const uint32_t o = c.pos - w.pos;
+    const uint32_t e = o == 0u ? w.v.x : (o == 1u ? w.v.y : (o == 2u ? w.v.z : (o == 3u ? w.v.w : esc_global(esc, c.pos))));
+    const uint32_t ek = e >> 16;
+    if (ek >= k0 + kChunkK) break;
+    if (ek >= k0) patch16(d, ek - k0, e & 0xFFFFu);
+    ++c.pos;
+  }
+}
+
+// Cursors of the lane's kRB lists at their first entry with k >= k_lo: the kRB binary searches
+// run in lockstep, one round of loads per halving (entries through the buffer resource, so a
+// finished search's probe reads nothing past E).
+__device__ __forceinline__ void esc_start_lists(__amdgpu_buffer_rsrc_t re, const uint32_t lo[kRB],
+                                                const uint32_t hi[kRB], uint32_t k_lo, LaneEsc c[kRB]) {
+  uint32_t a[kRB], b[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    a[rb] = lo[rb];
+    b[rb] = hi[rb];
+    c[rb].end = hi[rb];
+  }
+  for (;;) {
+    bool open = false;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) open = open || a[rb] < b[rb];
+    if (!__builtin_amdgcn_ballot_w64(open)) break;
+    uint32_t mid[kRB], v[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      mid[rb] = a[rb] + ((b[rb] - a[rb]) >> 1);
+      v[rb] = __builtin_amdgcn_raw_buffer_load_b32(re, (int)(a[rb] < b[rb] ? mid[rb] * 4u : kOutOfRange), 0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      if (a[rb] < b[rb]) {
+        if ((v[rb] >> 16) < k_lo) a[rb] = mid[rb] + 1;
+        else b[rb] = mid[rb];
+      }
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) c[rb].pos = a[rb];
+}
+
 // Per-lane geometry of one segment (the stretch of one tile inside a work-group's range).
 struct SegGeo {
   int64_t u, seg_end, tile, t0, rg;   // tile: index within its product; u, seg_end, t0: launch units
@@ -736,15 +820,25 @@ __device__ __forceinline__ void wait_pending3(int pend) {
   else wait_vmcnt<0>();
 }
 
-template <int V>
+// W: the escape windows' loads, issued after every stage and before its wait (dense
+// instantiation), or 0.
+template <int V, int W = 0>
 __device__ __forceinline__ void wait_pending(int pend) {
   constexpr int E = 2 * kRB;
-  if (pend == V + E) wait_vmcnt<V + E>();
-  else if (pend == V + 1) wait_vmcnt<V + 1>();
-  else if (pend == V) wait_vmcnt<V>();
-  else if (pend == E) wait_vmcnt<E>();
-  else if (pend == 1) wait_vmcnt<1>();
-  else wait_vmcnt<0>();
+  if constexpr (W == 0) {
+    if (pend == V + E) wait_vmcnt<V + E>();
+    else if (pend == V + 1) wait_vmcnt<V + 1>();
+    else if (pend == V) wait_vmcnt<V>();
+    else if (pend == E) wait_vmcnt<E>();
+    else if (pend == 1) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
+  } else {
+    if (pend == V + E + W) wait_vmcnt<V + E + W>();
+    else if (pend == V + W) wait_vmcnt<V + W>();
+    else if (pend == E + W) wait_vmcnt<E + W>();
+    else if (pend == W) wait_vmcnt<W>();
+    else wait_vmcnt<0>();
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -753,7 +847,8 @@ __device__ __forceinline__ void wait_pending(int pend) {
 // kQ: the Q pass of two-level verification (news article, two-level verification part): the
 // same GEMM on the nested 8-bit view, i.e. every in-window weight with its four low mantissa
 // bits zero (the lo plane is never read: its ring slots hold zeros) and escapes exact.
-template <class Path, bool kQ, int NG>
+// kDense: the instantiation for escape-dense tensors (escape windows, see EscWin).
+template <class Path, bool kQ, int NG, bool kDense = false>
 __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   constexpr int RB = kRB;
   constexpr int ROWS = kTileRows;
@@ -770,6 +865,8 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   // W stage fits in LDS.
   constexpr bool kW3 = Path::kWStages == 3;
   static_assert(!kW3 || Path::kXInLds, "three W stages need X in LDS");
+  static_assert(!kDense || (Path::kDenseOk && !kW3 && NG == 1 && !kQ), "escape windows: single 2-stage products");
+  constexpr int WW = kDense ? kRB : 0;   // escape-window loads between a stage and its wait
   constexpr int VW = kQ ? 4 : 6;   // W DMAs of a stage (the Q pass reads no lo plane)
   constexpr int VX = V - VW;       // X DMAs of a stage
   __shared__ RingStage<RB> ring0, ring1;
@@ -825,7 +922,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   // ---- prologue: the first segment's escape metadata and stage 0 (interleaved mapping
   // assumed), then the escape slice ----
   SegGeo cur;
-  seg_setup<Path>(g, gi_first, u_first, u_end, true, cur);
+  seg_setup<Path>(g, gi_first, u_first, u_end, !kDense, cur);
   uint4 xa0[Path::kAcc], xb0[Path::kAcc], xa1[Path::kAcc], xb1[Path::kAcc];
   auto issue_stage0 = [&]() {
     issue_w<RB, kQ>(g, rh, rl, cur.soff_h, cur.sl, 0, &ring0, wave);
@@ -838,13 +935,13 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   issue_stage0();
   uint32_t s0, s1;
   slice_range(g, cur.rg, se, s0, s1);   // waits for the escape loads only (stage 0 is newer)
-  if ((s1 - s0) > (uint32_t)kSliceEntries) {
+  if (!kDense && (s1 - s0) > (uint32_t)kSliceEntries) {
     // escape lists too long for LDS: contiguous mapping; stage 0 again (the first copy has landed)
     wait_vmcnt<0>();
     seg_setup<Path>(g, gi_first, u_first, u_end, false, cur);
     issue_stage0();
   }
-  issue_slice(re, s0, &slices[0][0], wave);
+  if constexpr (!kDense) issue_slice(re, s0, &slices[0][0], wave);
   if constexpr (kW3) {
     // and W stage 1, which stays in flight through the barrier
     if (cur.sl.iters > 1) {
@@ -860,15 +957,32 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   W12_TL(1);
 
   int sb = 0;   // slice buffer of the current segment
-  bool in_lds = (s1 - s0) <= (uint32_t)kSliceEntries;
+  bool in_lds = !kDense && (s1 - s0) <= (uint32_t)kSliceEntries;
   uint32_t bb2[RB];
   LaneEsc cur_esc[RB];
+  EscWin win[RB];   // dense instantiation only
+  // dense instantiation: the cursors of a segment and their first windows
+  auto dense_cursors = [&](const GemmArgs& gs, const SegEsc& es, __amdgpu_buffer_rsrc_t res) {
+    uint32_t lo[RB], hi[RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    uint32_t lo, hi;
-    seg_bounds(g, cur.rg, rb, se, lo, hi);
-    bb2[rb] = base_pair(se.base[rb] ? se.base[rb] : 1u);
-    esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, s0, slice_addr0);
+    for (int rb = 0; rb < RB; ++rb) {
+      seg_bounds(gs, cur.rg, rb, es, lo[rb], hi[rb]);
+      bb2[rb] = base_pair(es.base[rb] ? es.base[rb] : 1u);
+    }
+    esc_start_lists(res, lo, hi, cur.sl.c0 * kChunkK, cur_esc);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) load_win(res, cur_esc[rb], win[rb]);
+  };
+  if constexpr (kDense) {
+    dense_cursors(g, se, re);
+  } else {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      uint32_t lo, hi;
+      seg_bounds(g, cur.rg, rb, se, lo, hi);
+      bb2[rb] = base_pair(se.base[rb] ? se.base[rb] : 1u);
+      esc_start(cur_esc[rb], g, lo, hi, cur.sl.c0 * kChunkK, in_lds, s0, slice_addr0);
+    }
   }
   int npend = 0;   // partial tiles listed in s_pend (the first and last segment at most)
 
@@ -973,7 +1087,10 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     // stage j is complete once at most `pend` newer vector-memory instructions remain
     // (pend < 0: the caller has waited)
     auto compute = [&](uint32_t ah, uint32_t al, const XStage* xs, uint4* xa, uint4* xb, uint32_t j, int pend) {
-      if (pend >= 0) wait_pending<V>(pend);
+      if (pend >= 0) {
+        if constexpr (kDense) wait_pending<V, WW>(pend + WW);
+        else wait_pending<V>(pend);
+      }
       static_assert(RB == 4, "ring reads are written for 4 row blocks");
       uint4 h[RB];
       uint2 l[RB];
@@ -985,8 +1102,17 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
       for (int rb = 0; rb < RB; ++rb) {
         uint32_t d[8];
         decode16(h[rb], l[rb], bb2[rb], d);
-        if (valid) esc_apply(cur_esc[rb], g.esc, k0, d, in_lds, sl_addr);
+        if constexpr (kDense) {
+          if (valid) esc_apply_win(cur_esc[rb], win[rb], g.esc, k0, d, zero_records(d, bb2[rb]));
+        } else {
+          if (valid) esc_apply(cur_esc[rb], g.esc, k0, d, in_lds, sl_addr);
+        }
         Path::mac(d, xa, xb, acc[rb]);
+      }
+      if constexpr (kDense) {
+        // the next step's windows, before its stage is issued
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) load_win(r.e, cur_esc[rb], win[rb]);
       }
     };
     if constexpr (kW3) {
@@ -1057,7 +1183,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
         }
         pend = V;
       }
-      if (has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
+      if (!kDense && has_next && j == 0) {   // the next segment's escape slice (the compiler waits for the pairs)
         slice_range(ng, nrg, nse, ns0, ns1);
         issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
         next_sliced = true;
@@ -1069,7 +1195,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
 
     // ---- segment end ----
     if (tl_seg < 2) W12_TL(2 + 2 * tl_seg);
-    if (has_next && !next_sliced) {   // a one-step segment
+    if (!kDense && has_next && !next_sliced) {   // a one-step segment
       slice_range(ng, nrg, nse, ns0, ns1);
       issue_slice(nr.e, ns0, &slices[sb ^ 1][0], wave);
     }
@@ -1081,7 +1207,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     // in issue order, so the stores in between can only make a wait longer.
     SegGeo nx;
     if (has_next) {
-      seg_setup<Path>(ng, ngi, nu0, nu1, (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
+      seg_setup<Path>(ng, ngi, nu0, nu1, !kDense && (ns1 - ns0) <= (uint32_t)kSliceEntries, nx);
       issue_w<RB, kQ>(ng, nr.h, nr.l, nx.soff_h, nx.sl, 0, &ring0, wave);
       if constexpr (Path::kXInLds) Path::issue_x(ng, nr.x, nx.xc0, nx.xc_end, nx.sl.stride, nx.m0 * MROWS, 0, &xring0, wave);
       if constexpr (kW3) {
@@ -1153,13 +1279,17 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     // switch to the next segment
     cur = nx;
     sb ^= 1;
-    in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
+    if constexpr (kDense) {
+      dense_cursors(ng, nse, nr.e);
+    } else {
+      in_lds = (ns1 - ns0) <= (uint32_t)kSliceEntries;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      uint32_t lo, hi;
-      seg_bounds(ng, cur.rg, rb, nse, lo, hi);
-      bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
-      esc_start(cur_esc[rb], ng, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+      for (int rb = 0; rb < RB; ++rb) {
+        uint32_t lo, hi;
+        seg_bounds(ng, cur.rg, rb, nse, lo, hi);
+        bb2[rb] = base_pair(nse.base[rb] ? nse.base[rb] : 1u);
+        esc_start(cur_esc[rb], ng, lo, hi, cur.sl.c0 * kChunkK, in_lds, ns0, sb ? slice_addr1 : slice_addr0);
+      }
     }
   }
 
@@ -1170,10 +1300,10 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   W12_TL_VAL(13, (unsigned long long)tl_seg);
 }
 
-template <class Path, bool kQ>
+template <class Path, bool kQ, bool kDense = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
 void k_gemm(GroupArgs<1> ga) {
-  gemm_body<Path, kQ, 1>(ga);
+  gemm_body<Path, kQ, 1, kDense>(ga);
 }
 
 // Up to kGroupMax independent products of the same M in one launch.
@@ -1342,8 +1472,14 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
 }
 
 template <class Path, int NG>
-static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, hipStream_t stream) {
+static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, bool dense, hipStream_t stream) {
   if constexpr (NG == 1) {
+    if constexpr (Path::kDenseOk) {
+      if (dense && !qpass) {
+        hipLaunchKernelGGL((k_gemm<Path, false, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+        return;
+      }
+    }
     if (qpass) hipLaunchKernelGGL((k_gemm<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL((k_gemm<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
   } else {
@@ -1353,24 +1489,24 @@ static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, h
 }
 
 template <int NG>
-static void dispatch(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, hipStream_t stream) {
+static void dispatch(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, bool dense, hipStream_t stream) {
   if (p.path == 1) {
     switch (a.g[0].M) {
-      case 1: launch_path<GemvPath<1>>(p, a, qpass, stream); break;
-      case 2: launch_path<GemvPath<2>>(p, a, qpass, stream); break;
-      case 3: launch_path<GemvPath<3>>(p, a, qpass, stream); break;
-      case 4: launch_path<GemvPath<4>>(p, a, qpass, stream); break;
-      case 5: launch_path<GemvPath<5>>(p, a, qpass, stream); break;
-      case 6: launch_path<GemvPath<6>>(p, a, qpass, stream); break;
-      case 7: launch_path<GemvPath<7>>(p, a, qpass, stream); break;
-      default: launch_path<GemvPath<8>>(p, a, qpass, stream); break;
+      case 1: launch_path<GemvPath<1>>(p, a, qpass, dense, stream); break;
+      case 2: launch_path<GemvPath<2>>(p, a, qpass, dense, stream); break;
+      case 3: launch_path<GemvPath<3>>(p, a, qpass, dense, stream); break;
+      case 4: launch_path<GemvPath<4>>(p, a, qpass, dense, stream); break;
+      case 5: launch_path<GemvPath<5>>(p, a, qpass, dense, stream); break;
+      case 6: launch_path<GemvPath<6>>(p, a, qpass, dense, stream); break;
+      case 7: launch_path<GemvPath<7>>(p, a, qpass, dense, stream); break;
+      default: launch_path<GemvPath<8>>(p, a, qpass, dense, stream); break;
     }
   } else {
     switch (p.m_tile / 16) {
-      case 1: launch_path<MfmaPath<1>>(p, a, qpass, stream); break;
-      case 2: launch_path<MfmaPath<2>>(p, a, qpass, stream); break;
-      case 3: launch_path<MfmaPath<3>>(p, a, qpass, stream); break;
-      default: launch_path<MfmaPath<4>>(p, a, qpass, stream); break;
+      case 1: launch_path<MfmaPath<1>>(p, a, qpass, dense, stream); break;
+      case 2: launch_path<MfmaPath<2>>(p, a, qpass, dense, stream); break;
+      case 3: launch_path<MfmaPath<3>>(p, a, qpass, dense, stream); break;
+      default: launch_path<MfmaPath<4>>(p, a, qpass, dense, stream); break;
     }
   }
 }
@@ -1410,7 +1546,10 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   GroupArgs<1> ga;
   ga.g[0] = a;
   ga.count = 1;
-  dispatch(p, ga, qpass, stream);
+  // escape lists longer on average than the LDS slice of a 64-channel tile: the escape-window
+  // instantiation (where the path has one)
+  const bool dense = (uint64_t)t->num_escapes * kTileRows > (uint64_t)kSliceEntries * (uint64_t)t->N;
+  dispatch(p, ga, qpass, dense, stream);
   return hipGetLastError();
 }
 
@@ -1529,7 +1668,7 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
   }
   for (int i = count; i < kGroupMax; ++i) ga.g[i] = ga.g[0];   // never selected (count bounds gemm_of)
   ga.count = count;
-  dispatch(p, ga, qpass, stream);
+  dispatch(p, ga, qpass, false, stream);
   return hipGetLastError();
 }
 

@@ -12,7 +12,7 @@ import torch
 import lossless_bit_weight_encode_amd as w12
 import w12_synth as S
 from oracle import w12_oracle as O
-from gpu_util import assert_encode_equal, to_dev, u16, u32
+from gpu_util import assert_encode_equal, say, to_dev, u16, u32
 
 pytestmark = pytest.mark.gpu
 
@@ -504,3 +504,62 @@ def test_encode_many_matches_encode():
         for nm, t in zip(names, got):
             assert_encode_equal(t, case(nm)[1])
     assert w12.encode_many([]) == []
+
+
+# ---------------------------------------------------------------------------------------
+# Escape-dense tensors: more escapes per 64-channel tile than its LDS slice holds, on average.
+# The 16-row MFMA tiles and the GEMV (M <= 4) run an instantiation of their own for them that
+# keeps the next four entries of each list in registers and reads past them one at a time.
+
+
+def _dense_mix(seed, n, k):
+    """Heavy-tail rows (about 2% escapes), Gaussian rows (almost none) and rows of zeros (all
+    escapes): some tiles' lists fit a slice and some do not; n and k ragged."""
+    g = torch.Generator().manual_seed(seed)
+    w = S.layer_matrix(g, n, k)
+    w[:64] = S.heavy_tail_weights(seed, 64, k)
+    w[128:] = 0
+    return w
+
+
+def _window_edge(seed, n, k):
+    """Gaussian rows with (n + c) % 7 zeros at the start of chunk c of channel n: chunks with
+    0..6 escapes, i.e. inside, at and past a four-entry window."""
+    w = S.layer_matrix(torch.Generator().manual_seed(seed), n, k)
+    for r in range(n):
+        for c in range(k // 16):
+            w[r, 16 * c:16 * c + (r + c) % 7] = 0
+    return w
+
+
+DENSE = {
+    "dense_mix_150x1000": lambda: _dense_mix(31, 150, 1000),
+    "window_edge_64x512": lambda: _window_edge(32, 64, 512),
+}
+_dense_cache = {}
+
+
+@pytest.mark.parametrize("name", list(DENSE))
+@pytest.mark.parametrize("m,gemv_max,grid", [(1, 2, 0), (2, 2, 0), (3, 4, 0), (4, 4, 0), (8, 2, 0),
+                                              (16, 2, 0), (16, 2, 3), (1, 2, 2), (4, 4, 5)])
+def test_gemm_escape_dense(monkeypatch, name, m, gemv_max, grid):
+    """Escape-dense tensors through the escape-window instantiation (GEMV and 16-row tiles, some
+    with grids small enough that work-group ranges cross tiles): within tolerance of the FP64
+    product and bitwise repeatable."""
+    if name not in _dense_cache:
+        w = DENSE[name]()
+        _dense_cache[name] = (w, w12.encode(dev_weights(w)))
+    w, t = _dense_cache[name]
+    n, k = w.shape
+    assert t.num_escapes * 64 > 1024 * n, "the tensor must be escape-dense"
+    monkeypatch.setenv("W12_GEMV_MAX_M", str(gemv_max))
+    if grid:
+        monkeypatch.setenv("W12_MAX_GRID", str(grid))
+    say(f"[dense] {name} M={m} gemv_max={gemv_max} grid={grid} E={t.num_escapes}")
+    x = S.activations(m, k, 1300 + m)
+    xd = to_dev(x, (k + 7) // 8 * 8)
+    y1 = w12.gemm(xd, t).cpu().numpy()
+    y2 = w12.gemm(xd, t).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not bitwise repeatable"
+    bad, worst = O.gemm_check(x, w, y1)
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
