@@ -214,6 +214,7 @@ __device__ __forceinline__ void read_step(uint32_t ax, uint32_t ah, uint32_t al,
 // Escape cursor of one lane over one channel's list (slice-relative positions in LDS mode).
 struct WEsc {
   uint32_t pos, end, e;   // e: the entry at pos (valid when pos < end)
+  uint32_t nk;            // k of the entry at pos, all ones once the list is done
 };
 
 __device__ __forceinline__ void wesc_start(WEsc& c, const uint32_t* __restrict__ esc, uint32_t lo, uint32_t hi,
@@ -235,17 +236,23 @@ __device__ __forceinline__ void wesc_start(WEsc& c, const uint32_t* __restrict__
     c.end = hi;
     c.e = c.pos < c.end ? esc_global(esc, c.pos) : 0u;
   }
+  c.nk = c.pos < c.end ? c.e >> 16 : 0xFFFFFFFFu;
 }
 
 // Consume the entries of chunk [k16, k16 + 16); patch those in this lane's half
 // [k16 + 8 h, + 8) into its 4 decoded pairs.
 __device__ __forceinline__ void wesc_apply(WEsc& c, const uint32_t* __restrict__ esc, uint32_t k16, uint32_t kh,
                                            uint32_t d[4], bool in_lds, uint32_t slice_addr) {
-  while (c.pos < c.end && (c.e >> 16) < k16 + kChunkK) {
-    const uint32_t k = c.e >> 16;
+  while (c.nk < k16 + kChunkK) {
+    const uint32_t k = c.nk;
     if (k >= kh && k < kh + 8) patch_pairs<4>(d, k - kh, c.e & 0xFFFFu);
     ++c.pos;
-    if (c.pos < c.end) c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc_global(esc, c.pos);
+    if (c.pos < c.end) {
+      c.e = in_lds ? lds_read_u32(slice_addr + 4u * c.pos) : esc_global(esc, c.pos);
+      c.nk = c.e >> 16;
+    } else {
+      c.nk = 0xFFFFFFFFu;
+    }
   }
 }
 
@@ -349,10 +356,10 @@ void k_gemm_wide(WideArgs g) {
         wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave);
       }
       // one test per stage: does any lane of the wave hold an escape before the stage's end?
+      // (each cursor carries the k of its next entry; then one test per k16 step and channel
+      // block, so only the lists that have an entry there are walked)
       const uint32_t kend = (s.cs0 + 2 * j + 2) * kChunkK;
-      const bool pend = (cur[0].pos < cur[0].end && (cur[0].e >> 16) < kend) ||
-                        (cur[1].pos < cur[1].end && (cur[1].e >> 16) < kend);
-      const bool any_esc = __builtin_amdgcn_ballot_w64(pend) != 0;
+      const bool any_esc = __builtin_amdgcn_ballot_w64(min(cur[0].nk, cur[1].nk) < kend) != 0;
       const uint32_t so = slot * kStageBytes;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -367,7 +374,8 @@ void k_gemm_wide(WideArgs g) {
         if (any_esc && ck < s.cs1) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            wesc_apply(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb], in_lds, slice_addr);
+            if (__builtin_amdgcn_ballot_w64(cur[nb].nk < (ck + 1) * kChunkK) != 0)
+              wesc_apply(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb], in_lds, slice_addr);
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
