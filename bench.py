@@ -1343,13 +1343,14 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
     return out
 
 
-def kernel_name(plan, m):
-    """Name of the GEMM kernel variant a plan launches (exact pass), as rocprofv3 lists it."""
-    if plan["path"] == 1:
-        return f"w12::k_gemm<w12::GemvPath<{m}>, false>"
+def kernel_name(plan, m, dense=False):
+    """Name of the GEMM kernel variant a plan launches (exact pass), as rocprofv3 lists it; dense:
+    the escape-window instantiation that escape-dense tensors run (GEMV M <= 4, 16-row tiles)."""
     if plan["path"] == 3:
         return f"w12::k_gemm_wide<{plan['m_tile'] // 64}, false>"
-    return f"w12::k_gemm<w12::MfmaPath<{plan['m_tile'] // 16}>, false>"
+    path = f"GemvPath<{m}>" if plan["path"] == 1 else f"MfmaPath<{plan['m_tile'] // 16}>"
+    dense = dense and (m <= 4 if plan["path"] == 1 else plan["m_tile"] == 16)
+    return f"w12::k_gemm<w12::{path}, false, {'true' if dense else 'false'}>"
 
 
 def traffic_from_profile(alg):
@@ -1505,7 +1506,7 @@ def summarize_counters(fetch_csv, write_csv):
     src = os.path.join(ROOT, "lossless_bit_weight_encode_amd", "csrc", "w12_gemm.hip")
     with open(src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    out = {"kernel": "w12::k_gemm<w12::MfmaPath<1>> (M=16 launches of the layer step)",
+    out = {"kernel": "w12::k_gemm<w12::MfmaPath<1>, false, false> (M=16 launches of the layer step)",
            "dispatches": len(layer_gemms), "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "hbm_bytes_per_launch": fetch + write,
            "fetch_scale": res["FETCH_SIZE"]["scale"], "write_scale": res["WRITE_SIZE"]["scale"],
