@@ -181,6 +181,10 @@ def main():
                     help="turn a rocprofv3 --pmc run of --mfma-probe (SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) and the probe's own output into the "
                          "MFMA summary under profiles/")
+    ap.add_argument("--summarize-wide-lds", nargs=2, metavar=("PMC_CSV", "PROBE_JSON"),
+                    help="turn a rocprofv3 --pmc run of --mfma-probe (SQ_INSTS_LDS, SQ_LDS_BANK_CONFLICT, "
+                         "SQ_LDS_IDX_ACTIVE, SQ_WAIT_INST_LDS) and the probe's own output into the wide-tile LDS "
+                         "summary under profiles/")
     ap.add_argument("--valu-probe", action="store_true",
                     help="only gate_up at M=1, 8, 16, 32, 48 and 64 (three launches each on rotating copies), for "
                          "the VALU instruction and stall counters; prints their event times as JSON")
@@ -255,6 +259,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_wide_lds:
+        summarize_wide_lds(*args.summarize_wide_lds)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
@@ -1020,6 +1027,45 @@ def summarize_mfma(pmc_csv, probe_json):
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
+
+
+def summarize_wide_lds(pmc_csv, probe_json):
+    """LDS counters of the --mfma-probe wide-tile launches (summed over the GPU per dispatch; each
+    case is the middle of its three launches, in the probe's fixed launch order)."""
+    rows = _counter_rows(pmc_csv)
+    by_disp = {}
+    for r in rows:
+        if "k_gemm" not in r["Kernel_Name"]:
+            continue
+        d = by_disp.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [by_disp[i] for i in sorted(by_disp)]
+    command = ("rocprofv3 --pmc SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS -f csv "
+               "-d gpurun_out/pmc_lds -o run -- python3 bench.py --mfma-probe")
+    lines = ["# LDS counters of the wide-tile GEMM (batched verify, M = 256 / 512), MI355X", "",
+             "Command (run from the repository root), then the summary:", "", "```", command,
+             "python3 bench.py --mfma-probe > gpurun_out/mfma_probe.json",
+             f"python3 bench.py --summarize-wide-lds {pmc_csv} {probe_json}", "```", "",
+             f"Kernel sources: `csrc/` sha256 {source_stamp()}.", "",
+             "Counters are summed over the GPU; each row is the middle of the three launches of a case.", "",
+             "| case | kernel | SQ_INSTS_LDS | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | conflict / active | "
+             "SQ_WAIT_INST_LDS |", "|---|---|---|---|---|---|---|"]
+    i = 0
+    for nm in MFMA_PROBE_MATS:
+        for m in MFMA_PROBE_M:
+            mid = disp[i + 1]
+            i += 3
+            act = mid["SQ_LDS_IDX_ACTIVE"]
+            lines.append(f"| {nm} M={m} | `{mid['kernel'].split('(')[0]}` | {mid['SQ_INSTS_LDS']:.0f} | "
+                         f"{mid['SQ_LDS_BANK_CONFLICT']:.0f} | {act:.0f} | "
+                         f"{mid['SQ_LDS_BANK_CONFLICT'] / act if act else 0.0:.3f} | {mid['SQ_WAIT_INST_LDS']:.0f} |")
+    lines += ["", "SQ_INSTS_LDS is within 1.3% of 16 operand reads per wave and 32-k stage (4 X fragments, 2 hi "
+              "and 2 lo reads per k16 step, two steps), e.g. 21,760 work-group stages x 8 waves x 16 = 2.79 M for "
+              "gate_up at M = 256; the rest are escape-slice reads and the epilogue's."]
+    path = os.path.join(ROOT, "profiles", "gemm_wide_M256_M512_lds_counters.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize_valu(pmc_csv, probe_json):
