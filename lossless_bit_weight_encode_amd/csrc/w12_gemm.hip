@@ -8,7 +8,9 @@
 //     stage is in flight; the planes are read once and stream through L2), reads each
 //     lane's 16 + 8 bytes back, decodes them to BF16 pairs in registers (decode16) and
 //     patches the escapes of the lane's chunk from its channel's escape list, which sits in
-//     LDS (copied one segment ahead);
+//     LDS (copied one segment ahead); tensors whose lists do not fit there on average run an
+//     instantiation of their own that reads them from global memory through register windows
+//     (EscWin);
 //   * small M (the wavefront GEMV): FP32 dot2 (v_dot2c_f32_bf16) accumulation per lane, a
 //     fixed butterfly over the 4 lane groups and a fixed wave order through LDS; X rides the
 //     ring;

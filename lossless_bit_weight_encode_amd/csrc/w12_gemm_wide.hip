@@ -256,6 +256,38 @@ __device__ __forceinline__ void wesc_apply(WEsc& c, const uint32_t* __restrict__
   }
 }
 
+// Escape-dense tensors (lists longer than the LDS slice on average) run an instantiation of
+// their own.  There every list is walked in global memory, and a cursor's next entry read on the
+// spot waits for every load in flight (loads complete in issue order), which would drain the
+// ring at nearly every step.  Instead each stage's DMAs also gather, for each of the tile's 256
+// channels, the kWWin entries from the channel's cursor as it stands when the stage is issued
+// (the wave of row half wm takes the channels of block nb = wm, 16 bytes per lane); the entries
+// a stage needs are then in its window unless the channel holds more than kWWin entries in the
+// stages in flight, and only those are read from global memory.
+constexpr int kWWin = 8;   // entries per channel gathered with each stage (two 16-byte halves)
+
+__device__ __forceinline__ void lds_write_u32_w(uint32_t a, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1\ns_waitcnt lgkmcnt(0)" : : "v"(a), "v"(v) : "memory");
+}
+
+// wesc_apply with the next entries from the stage's window: win is the channel's window
+// (entries 0-3 at win, 4-7 at win + 512), wp the list position of its first entry.
+__device__ __forceinline__ void wesc_apply_win(WEsc& c, const uint32_t* __restrict__ esc, uint32_t k16, uint32_t kh,
+                                               uint32_t d[4], uint32_t win, uint32_t wp) {
+  while (c.nk < k16 + kChunkK) {
+    const uint32_t k = c.nk;
+    if (k >= kh && k < kh + 8) patch_pairs<4>(d, k - kh, c.e & 0xFFFFu);
+    ++c.pos;
+    if (c.pos < c.end) {
+      const uint32_t o = c.pos - wp;   // the cursor never moves back past the window's start
+      c.e = o < (uint32_t)kWWin ? lds_read_u32(win + (o >= 4u ? 512u : 0u) + 4u * (o & 3u)) : esc_global(esc, c.pos);
+      c.nk = c.e >> 16;
+    } else {
+      c.nk = 0xFFFFFFFFu;
+    }
+  }
+}
+
 // Output element (i, nb, r) of this lane: row and channel inside the tile.
 template <int TM>
 __device__ __forceinline__ int out_row(int wm, int i, int r, int lane) {
@@ -264,15 +296,21 @@ __device__ __forceinline__ int out_row(int wm, int i, int r, int lane) {
 __device__ __forceinline__ int out_col(int wn, int nb, int lane) { return 64 * wn + 32 * nb + (lane & 31); }
 
 // kQ: the Q pass on the nested 8-bit view (lo plane never read: zero nibbles; escapes exact).
-template <int TM, bool kQ>
+// kDense: the instantiation for escape-dense tensors (escape windows gathered with each stage,
+// a ring of 4 stages to make room for them).
+template <int TM, bool kQ, bool kDense = false>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void k_gemm_wide(WideArgs g) {
   typedef WideCfg<TM> C;
-  constexpr int NS = C::kNS;
-  constexpr int V_LO = C::kXDma + 1 + (kQ ? 0 : 1);   // DMAs per stage of waves 0-3
-  constexpr int V_NL = C::kXDma + 1;                  // of waves 4-7
+  static_assert(!(kDense && kQ), "escape windows: exact pass only");
+  constexpr int NS = kDense ? 4 : C::kNS;
+  constexpr int VW = kDense ? 1 : 0;                       // the window DMA of a stage
+  constexpr int V_LO = C::kXDma + 1 + (kQ ? 0 : 1) + VW;   // DMAs per stage of waves 0-3
+  constexpr int V_NL = C::kXDma + 1 + VW;                  // of waves 4-7
   __shared__ WideStage<TM> ring[NS];
-  __shared__ uint32_t slice[kWSlice];
+  __shared__ uint32_t slice[kDense ? 4 : kWSlice];
+  __shared__ uint4 wwin[kDense ? NS : 1][kWCols / 32][kWave];   // [stage][block of 32 channels][half, channel]
+  __shared__ uint32_t wwpos[kDense ? NS : 1][kWCols];          // [stage][channel]: list position of the window
   __shared__ uint32_t s_last;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int wm = wave >> 2, wn = wave & 3;
@@ -306,7 +344,7 @@ void k_gemm_wide(WideArgs g) {
     uint32_t s0 = __builtin_amdgcn_readfirstlane(g.esc_ptr[s.n0]);
     s1 = s1 < g.num_esc ? s1 : g.num_esc;
     s0 = s0 < s1 ? s0 : s1;
-    const bool in_lds = (s1 - s0) <= (uint32_t)kWSlice;
+    const bool in_lds = !kDense && (s1 - s0) <= (uint32_t)kWSlice;
     uint32_t elo[2], ehi[2], bb2[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -324,16 +362,34 @@ void k_gemm_wide(WideArgs g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)&slice[wave * kWave * 4], 16,
                                                (int)((s0 + (uint32_t)(wave * kWave * 4 + lane * 4)) * 4u), 0, 0, 0);
     }
+    WEsc cur[2];
+    if constexpr (kDense) {   // global-memory cursors, before the stages (their windows start there)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) wesc_start(cur[nb], g.esc, elo[nb], ehi[nb], s.cs0 * kChunkK, false, s0, slice_addr);
+    }
+    // the window of a stage: this wave's channel block nb = wm, from each cursor as it stands
+    auto issue_win = [&](uint32_t slot_w) {
+      if constexpr (kDense) {
+        const uint32_t pos = wm ? cur[1].pos : cur[0].pos;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)&wwin[slot_w][2 * wn + wm][0], 16,
+                                                 (int)((pos + 4u * hsel) * 4u), 0, 0, 0);
+        if (lane < 32) lds_write_u32_w(lds_off(&wwpos[slot_w][64 * wn + 32 * wm + lane]), pos);
+      }
+    };
     // ---- the first NS - 1 stages ----
     WDma dm;
     wdma_setup<TM>(g, s, wave, lane, dm);
     const uint32_t nch = s.cs1 - s.cs0;
-    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave);
+    for (uint32_t j = 0; j < (uint32_t)(NS - 1) && j < s.nst; ++j) {
+      wide_issue<TM, kQ>(rx, rh, rl, dm, j, nch, &ring[j], wave);
+      issue_win(j);
+    }
     wait_vm_all();
     barrier();
-    WEsc cur[2];
+    if constexpr (!kDense) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) wesc_start(cur[nb], g.esc, elo[nb], ehi[nb], s.cs0 * kChunkK, in_lds, s0, slice_addr);
+      for (int nb = 0; nb < 2; ++nb) wesc_start(cur[nb], g.esc, elo[nb], ehi[nb], s.cs0 * kChunkK, in_lds, s0, slice_addr);
+    }
 
     f32x16 acc[TM][2];
 #pragma unroll
@@ -354,6 +410,7 @@ void k_gemm_wide(WideArgs g) {
       if (j + NS - 1 < s.nst) {
         const uint32_t ws = slot == 0 ? NS - 1 : slot - 1;
         wide_issue<TM, kQ>(rx, rh, rl, dm, j + NS - 1, nch, &ring[ws], wave);
+        issue_win(ws);
       }
       // one test per stage: does any lane of the wave hold an escape before the stage's end?
       // (each cursor carries the k of its next entry; then one test per k16 step and channel
@@ -374,8 +431,15 @@ void k_gemm_wide(WideArgs g) {
         if (any_esc && ck < s.cs1) {
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            if (__builtin_amdgcn_ballot_w64(cur[nb].nk < (ck + 1) * kChunkK) != 0)
-              wesc_apply(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb], in_lds, slice_addr);
+            if (__builtin_amdgcn_ballot_w64(cur[nb].nk < (ck + 1) * kChunkK) != 0) {
+              if constexpr (kDense) {
+                const uint32_t cw = 64 * wn + 32 * nb + (lane & 31);
+                wesc_apply_win(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb],
+                               lds_off(&wwin[slot][2 * wn + nb][lane & 31]), lds_read_u32(lds_off(&wwpos[slot][cw])));
+              } else {
+                wesc_apply(cur[nb], g.esc, ck * kChunkK, ck * kChunkK + 8 * hsel, d[nb], in_lds, slice_addr);
+              }
+            }
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
@@ -571,11 +635,16 @@ hipError_t launch_gemm_wide(const GemmPlan& p, const uint16_t* X, int32_t M, int
   a.P = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes);
   a.p_bytes = (uint32_t)p.partial_bytes;
   const dim3 grid((unsigned)p.grid), block(kWThreads);
+  // escape lists longer on average than the LDS slice of a 256-channel tile: the escape-window
+  // instantiation (exact pass)
+  const bool dense = !qpass && (uint64_t)t->num_escapes * kWCols > (uint64_t)kWSlice * (uint64_t)t->N;
   if (p.m_tile <= 128) {
     if (qpass) hipLaunchKernelGGL((k_gemm_wide<2, true>), grid, block, 0, stream, a);
+    else if (dense) hipLaunchKernelGGL((k_gemm_wide<2, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_gemm_wide<2, false>), grid, block, 0, stream, a);
   } else {
     if (qpass) hipLaunchKernelGGL((k_gemm_wide<4, true>), grid, block, 0, stream, a);
+    else if (dense) hipLaunchKernelGGL((k_gemm_wide<4, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((k_gemm_wide<4, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();

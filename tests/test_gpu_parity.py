@@ -563,3 +563,29 @@ def test_gemm_escape_dense(monkeypatch, name, m, gemv_max, grid):
     assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not bitwise repeatable"
     bad, worst = O.gemm_check(x, w, y1)
     assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
+
+
+@pytest.mark.parametrize("name", list(DENSE))
+@pytest.mark.parametrize("m,grid", [(65, 0), (200, 0), (300, 0), (130, 1), (257, 2)])
+def test_gemm_wide_escape_dense(monkeypatch, name, m, grid):
+    """Escape-dense tensors through the wide tiles' escape-window instantiation (W12_WIDE_MIN_M = 3
+    keeps every M on the wide tiles; small grids make work-group ranges cross tiles): within
+    tolerance of the FP64 product and bitwise repeatable."""
+    if name not in _dense_cache:
+        w = DENSE[name]()
+        _dense_cache[name] = (w, w12.encode(dev_weights(w)))
+    w, t = _dense_cache[name]
+    n, k = w.shape
+    assert t.num_escapes * 256 > 2048 * n, "the tensor must be escape-dense for 256-channel tiles"
+    monkeypatch.setenv("W12_WIDE_MIN_M", "3")
+    if grid:
+        monkeypatch.setenv("W12_MAX_GRID", str(grid))
+    assert w12.gemm_plan(m, n, k)["path"] == 3
+    say(f"[dense wide] {name} M={m} grid={grid} E={t.num_escapes}")
+    x = S.activations(m, k, 1700 + m)
+    xd = to_dev(x, (k + 7) // 8 * 8)
+    y1 = w12.gemm(xd, t).cpu().numpy()
+    y2 = w12.gemm(xd, t).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "not bitwise repeatable"
+    bad, worst = O.gemm_check(x, w, y1)
+    assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
