@@ -1391,9 +1391,10 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
 
 def kernel_name(plan, m, dense=False):
     """Name of the GEMM kernel variant a plan launches (exact pass), as rocprofv3 lists it; dense:
-    the escape-window instantiation that escape-dense tensors run (GEMV M <= 4, 16-row tiles)."""
+    the escape-window instantiation that escape-dense tensors run (GEMV M <= 4, 16-row tiles, wide
+    tiles)."""
     if plan["path"] == 3:
-        return f"w12::k_gemm_wide<{plan['m_tile'] // 64}, false>"
+        return f"w12::k_gemm_wide<{plan['m_tile'] // 64}, false, {'true' if dense else 'false'}>"
     path = f"GemvPath<{m}>" if plan["path"] == 1 else f"MfmaPath<{plan['m_tile'] // 16}>"
     dense = dense and (m <= 4 if plan["path"] == 1 else plan["m_tile"] == 16)
     return f"w12::k_gemm<w12::{path}, false, {'true' if dense else 'false'}>"
