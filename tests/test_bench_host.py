@@ -106,3 +106,21 @@ def test_summarize_stalls_arithmetic(tmp_path, monkeypatch):
     assert c["wait_inst_issue_frac"] == pytest.approx(4 * 125_000 / 5e6)
     assert c["active_inst_frac"] == pytest.approx(1_000_000 / 5e6)
     assert c["lds_conflict_over_active"] == pytest.approx(0.25)
+
+
+def test_kernel_names_match_the_instantiations():
+    """The kernel names the benchmark reports are the ones rocprofv3 lists: the streaming kernel
+    with its (Q pass, escape-window) flags, the window flag only where the path has that
+    instantiation (GEMV M <= 4, 16-row tiles, wide tiles)."""
+    gemv = {"path": 1, "m_tile": 1}
+    assert B.kernel_name(gemv, 1) == "w12::k_gemm<w12::GemvPath<1>, false, false>"
+    assert B.kernel_name(gemv, 2, dense=True) == "w12::k_gemm<w12::GemvPath<2>, false, true>"
+    assert B.kernel_name(gemv, 6, dense=True) == "w12::k_gemm<w12::GemvPath<6>, false, false>"
+    m16 = {"path": 2, "m_tile": 16}
+    assert B.kernel_name(m16, 16) == "w12::k_gemm<w12::MfmaPath<1>, false, false>"
+    assert B.kernel_name(m16, 9, dense=True) == "w12::k_gemm<w12::MfmaPath<1>, false, true>"
+    m32 = {"path": 2, "m_tile": 32}
+    assert B.kernel_name(m32, 32, dense=True) == "w12::k_gemm<w12::MfmaPath<2>, false, false>"
+    wide = {"path": 3, "m_tile": 256}
+    assert B.kernel_name(wide, 512) == "w12::k_gemm_wide<4, false, false>"
+    assert B.kernel_name({"path": 3, "m_tile": 128}, 100, dense=True) == "w12::k_gemm_wide<2, false, true>"
