@@ -112,8 +112,8 @@ int w12_decode(const w12_tensor *t, uint16_t *out, int64_t ldo, hipStream_t stre
  * Load-time bit-for-bit check (summary page result bullet of section 4.1).  Decodes t and
  * compares with ref (row pitch ldr).  Writes, on the device,
  *   d_result[0] = number of positions (n,k) whose decoded bits differ from ref[n][k]
- *                 plus the number of malformed escape entries (k >= K, k not strictly
- *                 ascending within a channel, non-zero record under an escape) plus
+ *                 plus the number of malformed escape entries (k >= K, k not above the k
+ *                 of the entry before it in its channel, non-zero record under an escape) plus
  *                 the number of inconsistent pointers (esc_ptr[0] != 0, a decreasing
  *                 step, esc_ptr[N] != num_escapes);
  *   d_result[1] = smallest flat index n*K + k of a differing position, or

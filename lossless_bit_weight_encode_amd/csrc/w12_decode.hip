@@ -10,8 +10,11 @@ namespace w12 {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecChunksPerTask = 64;   // 1024 k per wave task, 16 chunks per lane
+constexpr int kDecMinChunks = 16;       // shortest task (4 chunks per lane)
+constexpr int64_t kDecMinTasks = 4096;  // tasks below which they are shortened (about 4 waves per SIMD)
 
-// A wave decodes one row block over a range of chunks.  Lane (r, g) owns row r and the
+// A wave decodes one row block over a range of cpt chunks (64, shortened down to 16 when a
+// small matrix would not give the GPU enough waves).  Lane (r, g) owns row r and the
 // chunks c0 + g, c0 + g + 4, ...: one load instruction covers 4 adjacent chunks (1 KB of hi)
 // and every row writes 128 contiguous bytes.  Escapes are applied through a per-lane cursor
 // over the row's list (entries of the other three lanes' chunks are stepped over).
@@ -19,15 +22,15 @@ template <bool kVerify>
 __global__ __launch_bounds__(kDecWaves * kWave) void k_decode(
     const uint8_t* __restrict__ base, const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
     const uint32_t* __restrict__ esc_ptr, const uint32_t* __restrict__ esc, uint32_t num_esc, int32_t N, int32_t K,
-    int64_t Kc, int64_t tasks_per_rb, int64_t num_tasks, uint16_t* __restrict__ out, const uint16_t* __restrict__ ref,
+    int64_t Kc, int64_t tasks_per_rb, int64_t num_tasks, int32_t cpt, uint16_t* __restrict__ out, const uint16_t* __restrict__ ref,
     int64_t ld, unsigned long long* __restrict__ result) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int64_t task = (int64_t)blockIdx.x * kDecWaves + wave;
   if (task >= num_tasks) return;
   const int64_t rb = task / tasks_per_rb;
-  const int64_t c_begin = (task % tasks_per_rb) * kDecChunksPerTask;
-  const int64_t c_end = (c_begin + kDecChunksPerTask < Kc) ? c_begin + kDecChunksPerTask : Kc;
+  const int64_t c_begin = (task % tasks_per_rb) * cpt;
+  const int64_t c_end = (c_begin + cpt < Kc) ? c_begin + cpt : Kc;
   const int64_t n = rb * kRowsPerBlock + r;
   const bool row_ok = n < N;
   const uint32_t b = row_ok ? base[n] : 1u;
@@ -100,40 +103,46 @@ __global__ void k_reset_result(unsigned long long* result) {
   }
 }
 
-// Structural check of the escape list, one thread per channel: pointers consistent, k < K,
-// k strictly ascending, and the record under each escape is the placeholder 0.
+// Structural check of the escape list: pointers consistent, k < K, k strictly ascending, and
+// the record under each escape is the placeholder 0.  L lanes per channel (a power of two up to
+// 64, from the average list length): lane j of a channel checks entries e_lo + j, + L, ...,
+// each against the entry before it; lane 0 checks the pointers.
 __global__ __launch_bounds__(256) void k_check_escapes(const uint8_t* __restrict__ hi, const uint8_t* __restrict__ lo,
                                                        const uint32_t* __restrict__ esc_ptr,
                                                        const uint32_t* __restrict__ esc, uint32_t num_esc, int32_t N,
-                                                       int32_t K, int64_t Kc, unsigned long long* __restrict__ result) {
-  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+                                                       int32_t K, int64_t Kc, int32_t lanes,
+                                                       unsigned long long* __restrict__ result) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = t / lanes;
+  const int j = (int)(t - n * lanes);
   uint32_t defects = 0;
-  const uint32_t a = esc_ptr[n], bnext = esc_ptr[n + 1];
-  if (bnext < a) ++defects;
-  if (bnext > num_esc) ++defects;
-  if (n == 0 && a != 0) ++defects;
-  if (n == N - 1 && bnext != num_esc) ++defects;
-  uint32_t e_lo, e_hi;
-  escape_range(esc_ptr, n, num_esc, e_lo, e_hi);
-  const int64_t rb = n / kRowsPerBlock;
-  const int r = (int)(n % kRowsPerBlock);
-  int64_t prev = -1;
-  for (uint32_t i = e_lo; i < e_hi; ++i) {
-    const uint32_t k = esc[i] >> 16;
-    if (k >= (uint32_t)K) {
-      ++defects;
-      continue;
+  if (n < N) {
+    const uint32_t a = esc_ptr[n], bnext = esc_ptr[n + 1];
+    if (j == 0) {
+      if (bnext < a) ++defects;
+      if (bnext > num_esc) ++defects;
+      if (n == 0 && a != 0) ++defects;
+      if (n == N - 1 && bnext != num_esc) ++defects;
     }
-    if ((int64_t)k <= prev) ++defects;
-    prev = k;
-    const int64_t c = k / kChunkK;
-    const int j = (int)(k % kChunkK);
-    const uint32_t hb = hi[hi_offset(rb, c, Kc, r) + j];
-    const int d = j >> 3, i4 = j & 7;
-    const uint32_t lb = lo[lo_offset(rb, c, Kc, r) + 4 * d + (i4 & 3)];
-    const uint32_t nib = (i4 < 4) ? (lb >> 4) : (lb & 0xFu);
-    if (hb != 0 || nib != 0) ++defects;
+    uint32_t e_lo, e_hi;
+    escape_range(esc_ptr, n, num_esc, e_lo, e_hi);
+    const int64_t rb = n / kRowsPerBlock;
+    const int r = (int)(n % kRowsPerBlock);
+    for (uint32_t i = e_lo + (uint32_t)j; i < e_hi; i += (uint32_t)lanes) {
+      const uint32_t k = esc[i] >> 16;
+      if (i > e_lo && k <= (esc[i - 1] >> 16)) ++defects;   // ascending within the channel
+      if (k >= (uint32_t)K) {
+        ++defects;
+        continue;
+      }
+      const int64_t c = k / kChunkK;
+      const int jj = (int)(k % kChunkK);
+      const uint32_t hb = hi[hi_offset(rb, c, Kc, r) + jj];
+      const int d = jj >> 3, i4 = jj & 7;
+      const uint32_t lb = lo[lo_offset(rb, c, Kc, r) + 4 * d + (i4 & 3)];
+      const uint32_t nib = (i4 < 4) ? (lb >> 4) : (lb & 0xFu);
+      if (hb != 0 || nib != 0) ++defects;
+    }
   }
   if (defects) atomicAdd(result, (unsigned long long)defects);
 }
@@ -159,9 +168,13 @@ __global__ __launch_bounds__(256) void k_unpack(const uint8_t* __restrict__ hi, 
   }
 }
 
-static void decode_grid(const w12_tensor* t, int64_t& tasks_per_rb, int64_t& num_tasks, unsigned& grid) {
+static void decode_grid(const w12_tensor* t, int64_t& tasks_per_rb, int64_t& num_tasks, unsigned& grid,
+                        int32_t& cpt) {
   const int64_t Kc = num_chunks(t->K);
-  tasks_per_rb = (Kc + kDecChunksPerTask - 1) / kDecChunksPerTask;
+  const int64_t nb = num_row_blocks(t->N);
+  cpt = kDecChunksPerTask;
+  while (cpt > kDecMinChunks && nb * ((Kc + cpt - 1) / cpt) < kDecMinTasks) cpt /= 2;
+  tasks_per_rb = (Kc + cpt - 1) / cpt;
   num_tasks = num_row_blocks(t->N) * tasks_per_rb;
   grid = (unsigned)((num_tasks + kDecWaves - 1) / kDecWaves);
 }
@@ -169,9 +182,10 @@ static void decode_grid(const w12_tensor* t, int64_t& tasks_per_rb, int64_t& num
 hipError_t launch_decode(const w12_tensor* t, uint16_t* out, int64_t ldo, hipStream_t stream) {
   int64_t tpr, nt;
   unsigned grid;
-  decode_grid(t, tpr, nt, grid);
+  int32_t cpt;
+  decode_grid(t, tpr, nt, grid, cpt);
   hipLaunchKernelGGL(k_decode<false>, dim3(grid), dim3(kDecWaves * kWave), 0, stream, t->base, t->hi, t->lo,
-                     t->esc_ptr, t->esc, (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), tpr, nt, out,
+                     t->esc_ptr, t->esc, (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), tpr, nt, cpt, out,
                      (const uint16_t*)nullptr, ldo, (unsigned long long*)nullptr);
   return hipGetLastError();
 }
@@ -183,15 +197,19 @@ hipError_t launch_verify(const w12_tensor* t, const uint16_t* ref, int64_t ldr, 
   if (e != hipSuccess) return e;
   int64_t tpr, nt;
   unsigned grid;
-  decode_grid(t, tpr, nt, grid);
+  int32_t cpt;
+  decode_grid(t, tpr, nt, grid, cpt);
   hipLaunchKernelGGL(k_decode<true>, dim3(grid), dim3(kDecWaves * kWave), 0, stream, t->base, t->hi, t->lo,
-                     t->esc_ptr, t->esc, (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), tpr, nt,
+                     t->esc_ptr, t->esc, (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), tpr, nt, cpt,
                      (uint16_t*)nullptr, ref, ldr, d_result);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned cgrid = (unsigned)((t->N + 255) / 256);
+  // lanes per channel: the average list length rounded up to a power of two, at most 64
+  int32_t lanes = 1;
+  while (lanes < 64 && (int64_t)lanes * t->N < t->num_escapes) lanes *= 2;
+  const unsigned cgrid = (unsigned)(((int64_t)t->N * lanes + 255) / 256);
   hipLaunchKernelGGL(k_check_escapes, dim3(cgrid), dim3(256), 0, stream, t->hi, t->lo, t->esc_ptr, t->esc,
-                     (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), d_result);
+                     (uint32_t)t->num_escapes, t->N, t->K, num_chunks(t->K), lanes, d_result);
   return hipGetLastError();
 }
 

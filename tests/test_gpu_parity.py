@@ -454,6 +454,31 @@ def test_gemm_large_m(m):
     assert bad == 0, f"{bad} outputs outside tolerance (worst rel {worst:.3g})"
 
 
+
+def test_verify_reports_corruption_escape_dense():
+    """The structural check on an escape-dense tensor, where it walks each channel's list with
+    64 lanes (entry i against entry i - 1): an entry moved past K and two entries swapped are
+    both reported, with the first differing position where an escape went missing."""
+    w, ref = case("all_escapes_20x96")
+    wd = to_dev(w, 96)
+    t = w12.encode(wd)
+    assert w12.verify(t, wd) == (0, -1)
+    esc0 = t.esc.clone()
+    n = 10
+    a, b = int(ref.esc_ptr[n]), int(ref.esc_ptr[n + 1])
+    assert b - a > 70, "the channel must hold more entries than one round of its 64 lanes"
+    i = a + 65   # the second entry of the second round of lanes
+    k_orig = int(ref.esc[i]) >> 16
+    t.esc[i] = int(((ref.k + 5) << 16) | (int(ref.esc[i]) & 0xFFFF))   # k past K
+    cnt, first = w12.verify(t, wd)
+    assert cnt >= 2 and first == n * ref.k + k_orig
+    t.esc.copy_(esc0)
+    t.esc[a + 64], t.esc[a + 65] = esc0[a + 65].clone(), esc0[a + 64].clone()   # out of order
+    cnt, _ = w12.verify(t, wd)
+    assert cnt >= 1
+    t.esc.copy_(esc0)
+    assert w12.verify(t, wd) == (0, -1)
+
 def test_side_stream_encode_verify_gemm():
     """Every binding call on a non-default stream: encode (its read-back of the escape count),
     verify (its read-back of the result) and the GEMM with its own workspace all run on that
