@@ -1333,16 +1333,25 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
             for nm in names:
                 w12.gemm(xs[S.LAYER_SHAPES[nm][1]], enc[nm], y=ys[nm], ws=wss[nm], stream=stream)
 
-    # grouped: `per` layers (4 per products) per launch
-    per = 2
-    wsg = w12.gemm_group_workspace(m, [model[0][nm] for nm in names] * per)
-    xg = [xs[S.LAYER_SHAPES[nm][1]] for nm in names] * per
-    yg = [torch.empty(m, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for nm in names * per]
+    # grouped: every product of the model in one launch (w12_gemm_group; the argument blocks go
+    # to the workspace), and, for comparison, 16 layers (64 products) and 2 layers (8 products,
+    # the kernel-argument form) per launch
+    ts_all = [enc[nm] for enc in model for nm in names]
+    xg = [xs[S.LAYER_SHAPES[nm][1]] for _ in model for nm in names]
+    yg = [torch.empty(m, S.LAYER_SHAPES[nm][0], dtype=torch.float32, device=dev) for _ in model for nm in names]
+    wsg = w12.gemm_group_workspace(m, ts_all)
 
     def grouped_pass():
-        for l0 in range(0, len(model), per):
-            ts = [model[l][nm] for l in range(l0, min(l0 + per, len(model))) for nm in names]
-            w12.gemm_group(xg[:len(ts)], ts, yg[:len(ts)], ws=wsg, stream=stream)
+        w12.gemm_group(xg, ts_all, yg, ws=wsg, stream=stream)
+
+    def by_layers(per):
+        wsp = w12.gemm_group_workspace(m, ts_all[:4 * per])
+
+        def run():
+            for l0 in range(0, len(ts_all), 4 * per):
+                w12.gemm_group(xg[l0:l0 + 4 * per], ts_all[l0:l0 + 4 * per], yg[l0:l0 + 4 * per], ws=wsp,
+                               stream=stream)
+        return run
 
     def time_pass(fn):
         fn()   # warm-up (code objects, first-touch of the outputs)
@@ -1360,6 +1369,7 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
 
     times = time_pass(one_pass)
     times_g = time_pass(grouped_pass)
+    times_by = {per: time_pass(by_layers(per)) for per in (16, 2) if per < len(model)}
     del flush
     t = float(np.median(times))
     t_g = float(np.median(times_g))
@@ -1377,13 +1387,21 @@ def full_model_leg(dev, stream, n_layers, m, reps=5):
         "encode_ms": round(t_enc, 3), "encode_GBps": round(wbytes / t_enc / 1e6, 1),
         "verify_ms": round(t_ver, 3), "verify_GBps": round((1.75 * wbytes + 4 * escapes) / t_ver / 1e6, 1),
         "grouped": {
-            "what": f"the same {4 * n_layers} products, {4 * per} per launch (w12_gemm_group, {per} layers each)",
+            "what": f"the same {4 * n_layers} products in one launch (w12_gemm_group)",
             "gemm_pass_ms_median": round(t_g, 4), "gemm_pass_ms_min": round(min(times_g), 4),
             "weight_GBps": round(wbytes / t_g / 1e6, 1), "bytes_moved_GBps": round(moved / t_g / 1e6, 1),
             "bytes_moved_frac_of_8TBps": round(moved / t_g / 1e6 / HBM_PEAK_GBPS, 4),
         },
     }
-    log(f"[bench] full model grouped pass M={m}: {t_g:.3f} ms, {moved / t_g / 1e6:.0f} GB/s moved")
+    for per, tp in times_by.items():
+        tm = float(np.median(tp))
+        out[f"grouped_by_{per}_layers"] = {
+            "what": f"the same {4 * n_layers} products, {4 * per} per launch (w12_gemm_group, {per} layers each)",
+            "gemm_pass_ms_median": round(tm, 4), "gemm_pass_ms_min": round(min(tp), 4),
+            "bytes_moved_frac_of_8TBps": round(moved / tm / 1e6 / HBM_PEAK_GBPS, 4),
+        }
+    log(f"[bench] full model grouped pass M={m}: {t_g:.3f} ms in one launch, {moved / t_g / 1e6:.0f} GB/s moved; " +
+        ", ".join(f"{np.median(tp):.3f} ms at {4 * per} products per launch" for per, tp in times_by.items()))
     del model
     torch.cuda.empty_cache()
     return out

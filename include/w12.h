@@ -202,9 +202,14 @@ int w12_gemm_noalloc(const uint16_t *X, int32_t M, int64_t ldx, const w12_tensor
  * the call returns W12_ERR_UNSUPPORTED_SHAPE.  items and the descriptors they point to are host
  * memory read during the call only.  ws: at least w12_gemm_group_workspace_size bytes,
  * initialised once with w12_gemm_workspace_init (counters at its start; every call leaves them
- * zero).  W12_GEMV_MAX_M, W12_GROUPS_PER_CU and W12_MAX_GRID apply as for w12_gemm.
+ * zero).  Up to W12_GROUP_INLINE products travel in the kernel arguments; a larger group (a
+ * whole model, say) first stores its per-product argument blocks (about 200 bytes each) at the
+ * end of the workspace, with one small kernel per W12_GROUP_INLINE products on `stream`, so the
+ * workspace of such a group carries that region too.  W12_GEMV_MAX_M, W12_GROUPS_PER_CU and
+ * W12_MAX_GRID apply as for w12_gemm.
  */
-#define W12_GROUP_MAX 8
+#define W12_GROUP_MAX 1024
+#define W12_GROUP_INLINE 8
 typedef struct w12_gemm_item {
   const uint16_t *X;     /* BF16 [M][ldx], device                                          */
   int64_t ldx;

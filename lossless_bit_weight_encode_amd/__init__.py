@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     encode_emit,
     encode_many,
     file_index,
+    GROUP_INLINE,
     GROUP_MAX,
     gemm,
     gemm_noalloc,

@@ -33,7 +33,8 @@ class _GemmItem(ctypes.Structure):
     _fields_ = [("X", _c_p), ("ldx", _c_i64), ("t", ctypes.POINTER(_Tensor)), ("Y", _c_p), ("ldy", _c_i64)]
 
 
-GROUP_MAX = 8
+GROUP_MAX = 1024      # products per grouped launch
+GROUP_INLINE = 8      # of which the kernel arguments hold this many; larger groups copy theirs to the workspace
 
 
 class _FileEntry(ctypes.Structure):

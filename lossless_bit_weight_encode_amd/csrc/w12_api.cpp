@@ -227,7 +227,7 @@ static int group_plan(int32_t M, int32_t count, const w12_gemm_item* items, w12:
     return fail(W12_ERR_UNSUPPORTED_SHAPE, "group of %d products outside 1..%d", count, W12_GROUP_MAX);
   if (M < 1 || M > 64) return fail(W12_ERR_UNSUPPORTED_SHAPE, "grouped M=%d outside 1..64", M);
   if (!items) return fail(W12_ERR_INVALID_ARG, "items is NULL");
-  int32_t N[W12_GROUP_MAX], K[W12_GROUP_MAX];
+  std::vector<int32_t> N((size_t)count), K((size_t)count);
   for (int i = 0; i < count; ++i) {
     int rc = check_tensor(items[i].t);
     if (rc) return item_fail(rc, i);
@@ -236,14 +236,14 @@ static int group_plan(int32_t M, int32_t count, const w12_gemm_item* items, w12:
     N[i] = items[i].t->N;
     K[i] = items[i].t->K;
   }
-  *plan = w12::plan_gemm_group(M, count, N, K, tiles_of, upt_of);
+  *plan = w12::plan_gemm_group(M, count, N.data(), K.data(), tiles_of, upt_of);
   return W12_OK;
 }
 
 int w12_gemm_group_workspace_size(int32_t M, int32_t count, const w12_gemm_item* items, uint64_t* bytes) {
   w12::GemmPlan p;
-  int64_t tiles_of[W12_GROUP_MAX], upt_of[W12_GROUP_MAX];
-  int rc = group_plan(M, count, items, &p, tiles_of, upt_of);
+  std::vector<int64_t> tiles_of(W12_GROUP_MAX), upt_of(W12_GROUP_MAX);
+  int rc = group_plan(M, count, items, &p, tiles_of.data(), upt_of.data());
   if (rc) return rc;
   if (!bytes) return fail(W12_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = p.ws_bytes;
@@ -253,8 +253,8 @@ int w12_gemm_group_workspace_size(int32_t M, int32_t count, const w12_gemm_item*
 static int gemm_group_call(int32_t M, int32_t count, const w12_gemm_item* items, void* ws, uint64_t ws_bytes,
                            bool qpass, hipStream_t stream) {
   w12::GemmPlan p;
-  int64_t tiles_of[W12_GROUP_MAX], upt_of[W12_GROUP_MAX];
-  int rc = group_plan(M, count, items, &p, tiles_of, upt_of);
+  std::vector<int64_t> tiles_of(W12_GROUP_MAX), upt_of(W12_GROUP_MAX);
+  int rc = group_plan(M, count, items, &p, tiles_of.data(), upt_of.data());
   if (rc) return rc;
   for (int i = 0; i < count; ++i) {
     const w12_gemm_item& it = items[i];
@@ -272,7 +272,7 @@ static int gemm_group_call(int32_t M, int32_t count, const w12_gemm_item* items,
                 (unsigned long long)p.ws_bytes);
   if (!ws) return fail(W12_ERR_INVALID_ARG, "ws is NULL");
   if (!aligned(ws, 16)) return fail(W12_ERR_MISALIGNED, "ws must be 16-byte aligned");
-  return hip_status(w12::launch_gemm_group(p, M, count, items, tiles_of, upt_of, ws, qpass, stream),
+  return hip_status(w12::launch_gemm_group(p, M, count, items, tiles_of.data(), upt_of.data(), ws, qpass, stream),
                     qpass ? "gemm_group_q" : "gemm_group");
 }
 

@@ -30,6 +30,7 @@
 // blocks.
 #include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "w12_device.h"
 #include "w12_gemm_common.h"
@@ -80,6 +81,38 @@ struct GroupArgs {
   int32_t count;
 };
 
+// More products than the kernel arguments hold (whole models in one launch): their arguments
+// sit in device memory, in the workspace after the partial tiles, in launch order.
+struct GroupArgsDev {
+  const GemmArgs* g;
+  int32_t count;
+};
+// The argument block of a launch: NG products in the kernel arguments, or (NG = 0) any number
+// in device memory.
+template <int NG>
+struct ArgsOf {
+  typedef GroupArgs<NG> type;
+};
+template <>
+struct ArgsOf<0> {
+  typedef GroupArgsDev type;
+};
+
+// Product i's argument block.  Device-memory blocks are read through the constant address
+// space (nothing writes them during the launch), as kernel arguments are: their loads stay
+// scalar, and the pointers loaded from them stay global (flat loads would also count on the LDS
+// wait counter).
+template <int NG, class I>
+__device__ __forceinline__ const GemmArgs& arg_at(const GroupArgs<NG>& ga, I i) {
+  return ga.g[i];
+}
+template <class I>
+__device__ __forceinline__ const GemmArgs& arg_at(const GroupArgsDev& ga, I i) {
+  typedef const __attribute__((address_space(4))) GemmArgs ConstArgs;
+  ConstArgs* p = (ConstArgs*)(uintptr_t)ga.g;
+  return *(const GemmArgs*)(p + i);
+}
+
 // The product that owns unit u (uniform).
 template <int NG>
 __device__ __forceinline__ int gemm_of(const GroupArgs<NG>& ga, int64_t u) {
@@ -89,6 +122,25 @@ __device__ __forceinline__ int gemm_of(const GroupArgs<NG>& ga, int64_t u) {
     for (int i = 1; i < NG; ++i)
       if (i < ga.count && u >= ga.g[i].ubase) gi = i;
   }
+  return gi;
+}
+__device__ __forceinline__ int gemm_of(const GroupArgsDev& ga, int64_t u) {
+  int lo = 0, hi = ga.count - 1;   // the last product whose first unit is <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (arg_at(ga, mid).ubase <= u) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+// The product that owns unit u, given that product gi owns an earlier unit (uniform).
+template <int NG>
+__device__ __forceinline__ int gemm_from(const GroupArgs<NG>& ga, int gi, int64_t u) {
+  (void)gi;
+  return gemm_of(ga, u);
+}
+__device__ __forceinline__ int gemm_from(const GroupArgsDev& ga, int gi, int64_t u) {
+  while (gi + 1 < ga.count && arg_at(ga, gi + 1).ubase <= u) ++gi;
   return gi;
 }
 
@@ -851,7 +903,7 @@ __device__ __forceinline__ void wait_pending(int pend) {
 // bits zero (the lo plane is never read: its ring slots hold zeros) and escapes exact.
 // kDense: the instantiation for escape-dense tensors (escape windows, see EscWin).
 template <class Path, bool kQ, int NG, bool kDense = false>
-__device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
+__device__ __forceinline__ void gemm_body(const typename ArgsOf<NG>::type& ga) {
   constexpr int RB = kRB;
   constexpr int ROWS = kTileRows;
   constexpr int MROWS = Path::kMRows;
@@ -886,12 +938,12 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   const int wave = wave_id();
   // units, G and P are launch-wide: the same in every member of a group
   const int64_t wg = logical_wg(blockIdx.x, gridDim.x);
-  const int64_t u_first = ubeg(ga.g[0], wg);
-  const int64_t u_end = ubeg(ga.g[0], wg + 1);
+  const int64_t u_first = ubeg(arg_at(ga, 0), wg);
+  const int64_t u_end = ubeg(arg_at(ga, 0), wg + 1);
   if (u_first >= u_end) return;
   const int gi_first = gemm_of(ga, u_first);
   // the first segment's product (the segment loop re-binds g and the resources per segment)
-  const GemmArgs& g = ga.g[gi_first];
+  const GemmArgs& g = arg_at(ga, gi_first);
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(g.hi, g.hi_bytes);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(g.lo, g.lo_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(g.X, g.x_bytes);
@@ -996,7 +1048,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     __syncthreads();
     W12_TL(14);
     if (threadIdx.x < (unsigned)npend) {
-      const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[threadIdx.x] : 0];
+      const GemmArgs& gt = arg_at(ga, NG != 1 ? s_pendg[threadIdx.x] : 0);
       const int64_t tile = s_pend[threadIdx.x];
       const int64_t t0 = gt.ubase + tile * gt.upt;
       const int64_t w_a = ceil_div((t0 + 1) * gt.G, gt.units) - 1;
@@ -1009,7 +1061,7 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
     W12_TL(15);
     for (int p = 0; p < npend; ++p) {
       if (!s_flag[p]) continue;
-      const GemmArgs& gt = ga.g[NG > 1 ? s_pendg[p] : 0];
+      const GemmArgs& gt = arg_at(ga, NG != 1 ? s_pendg[p] : 0);
       const int64_t tile = s_pend[p];
       const int64_t t0 = gt.ubase + tile * gt.upt;
       const int64_t w_a = ceil_div((t0 + 1) * gt.G, gt.units) - 1;
@@ -1067,14 +1119,14 @@ __device__ __forceinline__ void gemm_body(const GroupArgs<NG>& ga) {
   // wait looks past (stores and loads may complete out of order on the shared counter).
   for (;;) {
     // this segment's product and its operands (shadowing the prologue's)
-    const GemmArgs& g = ga.g[cur.gi];
+    const GemmArgs& g = arg_at(ga, cur.gi);
     const Res r = make_res(g);
     const __amdgpu_buffer_rsrc_t rh = r.h, rl = r.l, rx = r.x, ry = r.y;
     // the next segment: the rest of the range, possibly in the next product
     const int64_t nu0 = cur.seg_end, nu1 = u_end;
     const bool has_next = nu0 < nu1;
-    const int ngi = has_next ? gemm_of(ga, nu0) : cur.gi;
-    const GemmArgs& ng = ga.g[ngi];
+    const int ngi = has_next ? gemm_from(ga, cur.gi, nu0) : cur.gi;
+    const GemmArgs& ng = arg_at(ga, ngi);
     const Res nr = make_res(ng);
     const int64_t nrg = has_next ? ((nu0 - ng.ubase) / ng.upt) / ng.MT : 0;
     SegEsc nse;
@@ -1315,6 +1367,24 @@ void k_gemm_group(GroupArgs<kGroupMax> ga) {
   gemm_body<Path, kQ, kGroupMax>(ga);
 }
 
+// Any number of products, their arguments in device memory.
+template <class Path, bool kQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Path::kWavesPerEU)))
+void k_gemm_group_dev(GroupArgsDev ga) {
+  gemm_body<Path, kQ, 0>(ga);
+}
+
+static_assert(kGroupMax == W12_GROUP_INLINE, "the kernel-argument group size is part of the C ABI");
+
+// Stores the argument blocks of up to kGroupMax products (kernel arguments) to device memory.
+__global__ __launch_bounds__(256) void k_put_args(GroupArgs<kGroupMax> c, GemmArgs* __restrict__ dst) {
+  static_assert(sizeof(GemmArgs) % 4 == 0, "argument blocks are copied in 32-bit words");
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(&c.g[0]);
+  uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+  const int words = c.count * (int)(sizeof(GemmArgs) / 4);
+  for (int i = threadIdx.x; i < words; i += blockDim.x) d[i] = src[i];
+}
+
 __global__ __launch_bounds__(256) void k_zero_u32(uint32_t* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -1474,8 +1544,12 @@ GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K) {
 }
 
 template <class Path, int NG>
-static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, bool dense, hipStream_t stream) {
-  if constexpr (NG == 1) {
+static void launch_path(const GemmPlan& p, const typename ArgsOf<NG>::type& a, bool qpass, bool dense,
+                        hipStream_t stream) {
+  if constexpr (NG == 0) {
+    if (qpass) hipLaunchKernelGGL((k_gemm_group_dev<Path, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_gemm_group_dev<Path, false>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
+  } else if constexpr (NG == 1) {
     if constexpr (Path::kDenseOk) {
       if (dense && !qpass) {
         hipLaunchKernelGGL((k_gemm<Path, false, true>), dim3((unsigned)p.grid), dim3(kThreads), 0, stream, a);
@@ -1491,24 +1565,25 @@ static void launch_path(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, b
 }
 
 template <int NG>
-static void dispatch(const GemmPlan& p, const GroupArgs<NG>& a, bool qpass, bool dense, hipStream_t stream) {
+static void dispatch(const GemmPlan& p, int32_t M, const typename ArgsOf<NG>::type& a, bool qpass, bool dense,
+                     hipStream_t stream) {
   if (p.path == 1) {
-    switch (a.g[0].M) {
-      case 1: launch_path<GemvPath<1>>(p, a, qpass, dense, stream); break;
-      case 2: launch_path<GemvPath<2>>(p, a, qpass, dense, stream); break;
-      case 3: launch_path<GemvPath<3>>(p, a, qpass, dense, stream); break;
-      case 4: launch_path<GemvPath<4>>(p, a, qpass, dense, stream); break;
-      case 5: launch_path<GemvPath<5>>(p, a, qpass, dense, stream); break;
-      case 6: launch_path<GemvPath<6>>(p, a, qpass, dense, stream); break;
-      case 7: launch_path<GemvPath<7>>(p, a, qpass, dense, stream); break;
-      default: launch_path<GemvPath<8>>(p, a, qpass, dense, stream); break;
+    switch (M) {
+      case 1: launch_path<GemvPath<1>, NG>(p, a, qpass, dense, stream); break;
+      case 2: launch_path<GemvPath<2>, NG>(p, a, qpass, dense, stream); break;
+      case 3: launch_path<GemvPath<3>, NG>(p, a, qpass, dense, stream); break;
+      case 4: launch_path<GemvPath<4>, NG>(p, a, qpass, dense, stream); break;
+      case 5: launch_path<GemvPath<5>, NG>(p, a, qpass, dense, stream); break;
+      case 6: launch_path<GemvPath<6>, NG>(p, a, qpass, dense, stream); break;
+      case 7: launch_path<GemvPath<7>, NG>(p, a, qpass, dense, stream); break;
+      default: launch_path<GemvPath<8>, NG>(p, a, qpass, dense, stream); break;
     }
   } else {
     switch (p.m_tile / 16) {
-      case 1: launch_path<MfmaPath<1>>(p, a, qpass, dense, stream); break;
-      case 2: launch_path<MfmaPath<2>>(p, a, qpass, dense, stream); break;
-      case 3: launch_path<MfmaPath<3>>(p, a, qpass, dense, stream); break;
-      default: launch_path<MfmaPath<4>>(p, a, qpass, dense, stream); break;
+      case 1: launch_path<MfmaPath<1>, NG>(p, a, qpass, dense, stream); break;
+      case 2: launch_path<MfmaPath<2>, NG>(p, a, qpass, dense, stream); break;
+      case 3: launch_path<MfmaPath<3>, NG>(p, a, qpass, dense, stream); break;
+      default: launch_path<MfmaPath<4>, NG>(p, a, qpass, dense, stream); break;
     }
   }
 }
@@ -1551,7 +1626,7 @@ hipError_t launch_gemm(const GemmPlan& p, const uint16_t* X, int32_t M, int64_t 
   // escape lists longer on average than the LDS slice of a 64-channel tile: the escape-window
   // instantiation (where the path has one)
   const bool dense = (uint64_t)t->num_escapes * kTileRows > (uint64_t)kSliceEntries * (uint64_t)t->N;
-  dispatch(p, ga, qpass, dense, stream);
+  dispatch<1>(p, M, ga, qpass, dense, stream);
   return hipGetLastError();
 }
 
@@ -1630,14 +1705,16 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
   // most segments meeting one tile
   {
     int64_t best = 1, run_tile = -1, run = 0;
+    int i = 0;
+    int64_t ub = 0, gt = 0;   // first unit and first tile of product i (w's ranges only move forward)
     for (int64_t w = 1; w < G; ++w) {
-      int64_t u = w * p.units / G, gt = 0;
-      int i = 0;
-      while (u >= tiles_of[i] * upt_of[i]) {
-        u -= tiles_of[i] * upt_of[i];
+      const int64_t uw = w * p.units / G;
+      while (uw - ub >= tiles_of[i] * upt_of[i]) {
+        ub += tiles_of[i] * upt_of[i];
         gt += tiles_of[i];
         ++i;
       }
+      const int64_t u = uw - ub;
       if (u % upt_of[i] == 0) continue;
       const int64_t t = gt + u / upt_of[i];
       run = (t == run_tile) ? run + 1 : 1;
@@ -1649,13 +1726,41 @@ GemmPlan plan_gemm_group(int32_t M, int32_t count, const int32_t* N, const int32
   const uint64_t tile_elems = (uint64_t)p.rb * kRowsPerBlock * (uint64_t)p.m_tile;
   p.counter_bytes = kCounterBytes;
   p.partial_bytes = 2ull * (uint64_t)G * tile_elems * sizeof(float);
-  p.xpad_bytes = 0;
-  p.ws_bytes = p.counter_bytes + p.partial_bytes;
+  // more products than the kernel arguments hold: their argument blocks follow the partials
+  p.xpad_bytes = count > kGroupMax ? ((uint64_t)count * sizeof(GemmArgs) + 255) / 256 * 256 : 0;
+  p.ws_bytes = p.counter_bytes + p.partial_bytes + p.xpad_bytes;
   return p;
 }
 
 hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const w12_gemm_item* items,
                              const int64_t* tiles_of, const int64_t* upt_of, void* ws, bool qpass, hipStream_t stream) {
+  if (count > kGroupMax) {
+    // the arguments go to the workspace (after the partial tiles), copied on the stream
+    std::vector<GemmArgs> args((size_t)count);
+    int64_t ubase = 0;
+    for (int i = 0; i < count; ++i) {
+      GemmArgs& a = args[(size_t)i];
+      fill_args(a, p, items[i].X, M, items[i].ldx, items[i].t, items[i].Y, items[i].ldy, ws);
+      a.ubase = ubase;
+      a.tiles = tiles_of[i];
+      a.upt = upt_of[i];
+      a.units = p.units;
+      a.counters = reinterpret_cast<uint32_t*>(ws);
+      ubase += tiles_of[i] * upt_of[i];
+    }
+    // stored by kernels that take them by value, kGroupMax at a time (stream-ordered, and
+    // nothing on the host has to outlive the call)
+    GemmArgs* dev = reinterpret_cast<GemmArgs*>(reinterpret_cast<uint8_t*>(ws) + p.counter_bytes + p.partial_bytes);
+    for (int c0 = 0; c0 < count; c0 += kGroupMax) {
+      GroupArgs<kGroupMax> chunk{};
+      chunk.count = count - c0 < kGroupMax ? count - c0 : kGroupMax;
+      for (int j = 0; j < chunk.count; ++j) chunk.g[j] = args[(size_t)(c0 + j)];
+      hipLaunchKernelGGL(k_put_args, dim3(1), dim3(256), 0, stream, chunk, dev + c0);
+    }
+    GroupArgsDev ga{dev, count};
+    dispatch<0>(p, M, ga, qpass, false, stream);
+    return hipGetLastError();
+  }
   GroupArgs<kGroupMax> ga{};
   int64_t ubase = 0;
   for (int i = 0; i < count; ++i) {
@@ -1670,7 +1775,7 @@ hipError_t launch_gemm_group(const GemmPlan& p, int32_t M, int32_t count, const 
   }
   for (int i = count; i < kGroupMax; ++i) ga.g[i] = ga.g[0];   // never selected (count bounds gemm_of)
   ga.count = count;
-  dispatch(p, ga, qpass, false, stream);
+  dispatch<kGroupMax>(p, M, ga, qpass, false, stream);
   return hipGetLastError();
 }
 

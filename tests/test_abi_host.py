@@ -267,6 +267,39 @@ def test_gemm_group_workspace_covers_counters_and_partials(m):
     assert one.value <= need.value
 
 
+def test_group_constants_match_the_header():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define W12_GROUP_MAX (\d+)", text).group(1)) == L.GROUP_MAX
+    assert int(re.search(r"#define W12_GROUP_INLINE (\d+)", text).group(1)) == L.GROUP_INLINE
+    assert L.GROUP_INLINE < L.GROUP_MAX
+
+
+def _group_need(m, d):
+    need = L._c_u64()
+    rc = w12.lib().w12_gemm_group_workspace_size(m, len(d), _items(d, m), ctypes.byref(need))
+    return rc, need.value
+
+
+@pytest.mark.parametrize("m", [1, 16, 32])
+def test_large_group_workspace_holds_the_argument_blocks(m, monkeypatch):
+    """Past W12_GROUP_INLINE products the argument blocks (one per product) sit after the
+    partials: the region grows with the count, on top of what the same launch shape needs."""
+    monkeypatch.setenv("W12_MAX_GRID", "64")   # the same grid (and partial region) for every count
+    d = [_desc(n=64, k=2048) for _ in range(L.GROUP_MAX)]
+    sizes = {}
+    for count in (L.GROUP_INLINE, L.GROUP_INLINE + 1, 100, L.GROUP_MAX):
+        rc, sizes[count] = _group_need(m, d[:count])
+        assert rc == 0, count
+    inline = sizes[L.GROUP_INLINE]
+    # about 200 bytes per product, rounded to 256 bytes
+    for count in (L.GROUP_INLINE + 1, 100, L.GROUP_MAX):
+        extra = sizes[count] - inline
+        assert 64 * count <= extra <= 512 * count + 256, (count, extra)
+    assert (sizes[L.GROUP_MAX] - inline) % 256 == 0
+    rc, _ = _group_need(m, d + d[:1])
+    assert rc == -2
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     """Without libw12.so the binding raises; there is no other code path."""
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "absent" / "libw12.so"))

@@ -74,9 +74,17 @@ def run_group(names, m, seed, qpass=False, repeats=2):
     return xs, xd, ys
 
 
-# eight members (a full group), the no-escape one included; the size test cycles over all of them
+# eight members (a full group of the kernel-argument form), the no-escape one included; the size
+# test cycles over all of them
 ALL = [nm for nm in MEMBERS if nm != "wide_70x272"]
-assert len(ALL) == w12.GROUP_MAX
+assert len(ALL) == w12.GROUP_INLINE
+
+
+def many(count, step=5):
+    """count items cycling over every member (groups past GROUP_INLINE keep their arguments in
+    the workspace)."""
+    every = list(MEMBERS)
+    return [every[(step * i + i // len(every)) % len(every)] for i in range(count)]
 
 
 @pytest.mark.parametrize("m", [1, 2, 3, 8, 16, 17, 32, 33, 48, 64])
@@ -104,11 +112,50 @@ def test_group_qpass_within_tolerance(m):
     run_group(ALL, m, seed=300, qpass=True)
 
 
-def test_group_sizes_one_to_max():
-    for count in range(1, w12.GROUP_MAX + 1):
+def test_group_sizes_one_to_past_inline():
+    for count in range(1, w12.GROUP_INLINE + 4):
         every = list(MEMBERS)
         names = [every[(3 * i) % len(every)] for i in range(count)]
+        say(f"[group] count={count} M=16")
         run_group(names, 16, seed=400 + count, repeats=1)
+
+
+@pytest.mark.parametrize("count", [9, 33])
+@pytest.mark.parametrize("m", [1, 2, 16, 32, 40, 64])
+def test_large_group_within_tolerance(m, count):
+    """More products than the kernel arguments hold: the argument blocks go to the workspace."""
+    say(f"[group] count={count} M={m}")
+    run_group(many(count), m, seed=700 + count)
+
+
+@pytest.mark.parametrize("grid", [1, 2, 3, 7, 50])
+@pytest.mark.parametrize("m", [1, 16])
+def test_large_group_small_grids(monkeypatch, grid, m):
+    """Few work-groups over 20 products: one work-group's range walks across many products."""
+    monkeypatch.setenv("W12_MAX_GRID", str(grid))
+    say(f"[group] count=20 M={m} grid={grid}")
+    run_group(many(20), m, seed=800 + grid)
+
+
+@pytest.mark.parametrize("m", [5, 8])
+def test_large_group_gemv_path(monkeypatch, m):
+    monkeypatch.setenv("W12_GEMV_MAX_M", "8")
+    run_group(many(12), m, seed=850)
+
+
+@pytest.mark.parametrize("m", [1, 16, 33])
+def test_large_group_qpass_within_tolerance(m):
+    run_group(many(17), m, seed=900, qpass=True)
+
+
+def test_group_of_the_maximum_count():
+    """W12_GROUP_MAX products (small members) in one launch, twice, bitwise repeatable."""
+    small = ["single_1x16", "all_escapes_20x96", "wide_70x272", "wide_37x1008", "no_escapes_64x512"]
+    names = [small[i % len(small)] for i in range(w12.GROUP_MAX)]
+    say(f"[group] count={len(names)} M=16")
+    run_group(names, 16, seed=950)
+    with pytest.raises(w12.W12Error):
+        w12.gemm_group([to_dev(S.activations(1, 16, 1))] * (w12.GROUP_MAX + 1), [member("single_1x16")[1]] * (w12.GROUP_MAX + 1))
 
 
 @pytest.mark.parametrize("m", [1, 16, 64])
@@ -163,13 +210,45 @@ def test_group_layer_full_size(m):
         assert np.isfinite(yh).all()
 
 
+@pytest.mark.timeout(900)
+def test_group_whole_model_full_size():
+    """The launch the benchmark times for a 64-layer model at M=32: 256 products of decoder-layer
+    shapes in one launch (here layer 0's four matrices 64 times over, each with its own Y), on
+    sampled channels of every product, twice, bitwise repeatable."""
+    m, n_layers = 32, 64
+    lay = S.layer(0)
+    names = list(S.LAYER_ORDER)
+    enc = {nm: w12.encode(to_dev(lay[nm])) for nm in names}
+    xs = {nm: S.activations(m, S.LAYER_SHAPES[nm][1], S.x_seed(m, S.LAYER_SHAPES[nm][1])) for nm in names}
+    xd = {nm: to_dev(xs[nm]) for nm in names}
+    order = [nm for _ in range(n_layers) for nm in names]
+    ts = [enc[nm] for nm in order]
+    say(f"[group] whole model: {len(ts)} products M={m}")
+    ws = w12.gemm_group_workspace(m, ts)
+    ys = w12.gemm_group([xd[nm] for nm in order], ts, ws=ws)
+    torch.cuda.synchronize()
+    ys2 = w12.gemm_group([xd[nm] for nm in order], ts, ys=None, ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    for i, nm in enumerate(order):
+        assert torch.equal(ys[i], ys2[i]), f"item {i} ({nm}): not bitwise repeatable"
+        n = S.LAYER_SHAPES[nm][0]
+        rows = np.array(sorted(set(rng.choice(n, 24, replace=False).tolist()) | {0, n - 1}))
+        yh = ys[i].cpu().numpy()
+        bad, worst = O.gemm_check(xs[nm], lay[nm][rows], yh[:, rows])
+        assert bad == 0, f"item {i} ({nm}): {bad} sampled outputs outside tolerance (worst rel {worst:.3g})"
+        assert np.isfinite(yh).all()
+
+
 @pytest.mark.parametrize("m", [1, 16, 40])
-def test_group_deterministic_poisoned_workspace_and_canaries(monkeypatch, m):
-    """20 grouped launches bitwise identical, with the partial region of the workspace
-    NaN-poisoned before every launch (a read of a partial never written would show) and canary
-    values around every Y (nothing written outside Y).  A small grid makes most tiles split."""
+@pytest.mark.parametrize("count", [5, 13])
+def test_group_deterministic_poisoned_workspace_and_canaries(monkeypatch, m, count):
+    """20 grouped launches bitwise identical, with the partial region of the workspace (and the
+    argument blocks of a large group) NaN-poisoned before every launch (a read of a partial never
+    written would show) and canary values around every Y (nothing written outside Y).  A small
+    grid makes most tiles split."""
     monkeypatch.setenv("W12_MAX_GRID", "7")
-    names = ALL[:5]
+    names = many(count)
     ws_, ts, xs = [], [], []
     for i, nm in enumerate(names):
         w, t, _ = member(nm)
