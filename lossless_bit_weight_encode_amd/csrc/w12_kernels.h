@@ -38,9 +38,10 @@ struct GemmPlan {
   int64_t grid;        // work-groups G (resident at once); w takes units [w U / G, (w+1) U / G)
   uint64_t counter_bytes;  // kCounterBytes: the counter region at the start of the workspace
   uint64_t partial_bytes;  // two partial tiles per work-group
-  uint64_t xpad_bytes;     // X copied into the workspace: padded to whole 16-k chunks (K % 16 != 0),
-                           // or, for the wide tiles, rearranged into MFMA operand order
-  uint64_t ws_bytes;       // counters + partials + the copy of X
+  uint64_t xpad_bytes;     // the region after the partials: X copied into the workspace, padded to whole
+                           // 16-k chunks (K % 16 != 0) or, for the wide tiles, rearranged into MFMA operand
+                           // order; for a group past kGroupMax products, their argument blocks
+  uint64_t ws_bytes;       // counters + partials + that region
 };
 
 GemmPlan plan_gemm(int32_t M, int32_t N, int32_t K);
